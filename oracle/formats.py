@@ -44,15 +44,23 @@ def round_bf16(x: np.ndarray) -> np.ndarray:
 
 # ---------------------------------------------------------------- e4m3fn
 
+def _e4m3_value(c: int) -> float:
+    """Value of one e4m3fn code, from the field definitions."""
+    sign = -1.0 if c & 0x80 else 1.0
+    ex, man = (c >> 3) & 0xF, c & 0x7
+    if ex == 15 and man == 7:
+        return float("nan")
+    if ex == 0:
+        return sign * man * 2.0 ** -9
+    return sign * (1.0 + man / 8.0) * 2.0 ** (ex - 7)
+
+
+_E4M3_TABLE = np.array([_e4m3_value(c) for c in range(256)], np.float64)
+
+
 def e4m3_decode(codes: np.ndarray) -> np.ndarray:
-    """e4m3fn codes (uint8) -> exact values as float64."""
-    c = np.asarray(codes, np.uint8).astype(np.int64)
-    sign = np.where(c & 0x80, -1.0, 1.0)
-    ex = (c >> 3) & 0xF
-    man = (c & 0x7).astype(np.float64)
-    val = np.where(ex == 0, man * 2.0 ** -9, (1.0 + man / 8.0) * np.exp2(ex - 7.0))
-    val = np.where((ex == 15) & ((c & 7) == 7), np.nan, val)
-    return sign * val
+    """e4m3fn codes (uint8) -> exact values as float64 (table of all 256 codes)."""
+    return _E4M3_TABLE[np.asarray(codes, np.uint8)]
 
 
 def e4m3_encode(x: np.ndarray) -> np.ndarray:

@@ -244,20 +244,23 @@ def combine(out_rows: dict, slot_of: np.ndarray, weights: np.ndarray, y_dt: str,
 class ExpertWeights:
     """Dequantised (float64) expert weights, made on first use and cached."""
 
-    def __init__(self, cfg, w: dict):
-        self.cfg, self.w, self._c13, self._c2 = cfg, w, {}, {}
+    def __init__(self, cfg, w: dict, cache: bool = True):
+        self.cfg, self.w, self.cache, self._c13, self._c2 = cfg, w, cache, {}, {}
+
+    def _get(self, store: dict, name: str, e: int) -> np.ndarray:
+        if e in store:
+            return store[e]
+        sc = self.w.get(name + "_scales")
+        v = weight_values(self.w[name][e], self.cfg.wdt, None if sc is None else sc[e])
+        if self.cache:
+            store[e] = v
+        return v
 
     def w13(self, e: int) -> np.ndarray:
-        if e not in self._c13:
-            self._c13[e] = weight_values(self.w["w13"][e], self.cfg.wdt,
-                                         self.w.get("w13_scales", [None] * (e + 1))[e])
-        return self._c13[e]
+        return self._get(self._c13, "w13", e)
 
     def w2(self, e: int) -> np.ndarray:
-        if e not in self._c2:
-            self._c2[e] = weight_values(self.w["w2"][e], self.cfg.wdt,
-                                        self.w.get("w2_scales", [None] * (e + 1))[e])
-        return self._c2[e]
+        return self._get(self._c2, "w2", e)
 
 
 def expert_mlp_rows(cfg, a_vals_by_row: dict, expert_of_row: dict, ew: ExpertWeights) -> dict:
