@@ -1,0 +1,235 @@
+"""Benchmark of one GPU's MoE layer: dispatch layout -> permute (FP8) ->
+grouped W13 GEMM with fused SiLU*up -> grouped W2 GEMM -> combine.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload prefill_fp8]
+
+A step is one pass of the whole path over one batch of seeded synthetic
+input already resident in HBM.  Prints ONE JSON line with the metric,
+per-stage times, the dominant kernel's roofline (measured with HIP events on
+the stream the kernels run on) and the CPU oracle's throughput on a bounded
+sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+from pathlib import Path
+
+import numpy as np
+
+ROOT = Path(__file__).resolve().parent
+sys.path.insert(0, str(ROOT))
+
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
+MFMA_PEAK_TFLOPS = {"fp8": 5000.0, "bf16": 2500.0, "f32": 157.3}
+METRIC = "MoE layer token-expert rows/s + grouped-GEMM TFLOP/s (% MFMA peak), 1 GPU"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="prefill_fp8")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=2048)
+    ap.add_argument("--skip-cpu-baseline", action="store_true",
+                    help="omit the oracle timing (profiling runs)")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="run one plain device copy of this size first (counter calibration)")
+    return ap.parse_args()
+
+
+def algorithmic_work(cfg, counts):
+    """Bytes and FLOPs each kernel must move / compute at minimum.
+
+    Weights of experts with at least one row are read once; every valid row
+    of A, Z and the expert output is read or written once; padding rows do
+    not count."""
+    rows = int(counts.sum())
+    active = int((counts > 0).sum())
+    H, I = cfg.H, cfg.I
+    wb = {"fp8": 1, "bf16": 2, "f32": 4}[cfg.wdt]
+    ab = {"fp8": 1, "bf16": 2, "f32": 4}[cfg.buf_dt]
+    zb = {"fp8": 1, "bf16": 2, "f32": 4}[cfg.z_dt]
+    ob = {"bf16": 2, "f32": 4}[cfg.out_dt]
+    xb = {"bf16": 2, "f32": 4}[cfg.act]
+    fp8 = cfg.wdt == "fp8"
+    w13 = active * 2 * I * H * wb + (active * (2 * I // 128) * (H // 128) * 4 if fp8 else 0)
+    w2 = active * H * I * wb + (active * (H // 128) * (I // 128) * 4 if fp8 else 0)
+    a_bytes = rows * H * ab + (rows * (H // 128) * 4 if fp8 else 0)
+    z_bytes = rows * I * zb + (rows * (I // 128) * 4 if fp8 else 0)
+    out_bytes = rows * H * ob
+    return {
+        "rows": rows,
+        "w13_bytes": w13 + a_bytes + z_bytes,
+        "w13_flops": 2.0 * rows * H * 2 * I,
+        "w2_bytes": w2 + z_bytes + out_bytes,
+        "w2_flops": 2.0 * rows * I * H,
+        "gemm_flops": 6.0 * H * I * rows,
+    }
+
+
+def cpu_baseline(wl, n_tokens):
+    """The oracle, as is, on the first n_tokens tokens of the workload."""
+    from threadpoolctl import threadpool_info, threadpool_limits
+    from oracle import moe
+
+    cores = min(len(os.sched_getaffinity(0)), 16)
+    tokens = np.arange(min(n_tokens, wl.cfg.T))
+    with threadpool_limits(limits=cores):
+        blas = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+        t0 = time.perf_counter()
+        res = moe.moe_layer(wl, tokens=tokens, ew=moe.ExpertWeights(wl.cfg, wl.w, cache=False))
+        dt = time.perf_counter() - t0
+    rows = int((res["layout"]["slot_of"][tokens] >= 0).sum())
+    return {"value": rows / dt, "unit": "rows/s", "cores": int(blas), "kind": "oracle",
+            "sample": f"first {len(tokens)} of {wl.cfg.T} tokens ({rows} routed rows) of the same "
+                      f"workload through the whole numpy oracle (layout, FP8 permute, per-expert "
+                      f"weight dequantisation, fp64 GEMMs, combine); {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU's share of the MoE layer; --gpus {args.gpus} is not "
+              "supported (multi-GPU expert-parallel exchange is not part of this build)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import combine_top_expert_amd  # noqa: F401  (fails loudly without the HIP library)
+    from combine_top_expert_amd.pipeline import LayerShape, MoELayer
+    from workloads import get_config, make_workload
+
+    cfg = get_config(args.workload)
+    print(f"[bench] generating {cfg.name} inputs", file=sys.stderr, flush=True)
+    wl = make_workload(cfg)
+    shape = LayerShape(T=cfg.T, K=cfg.K, E=cfg.E, expert_begin=cfg.expert_begin, L=cfg.L, H=cfg.H,
+                       I=cfg.I, R=cfg.R, act=cfg.act, wdt=cfg.wdt)
+    dev = torch.device("cuda:0")
+
+    def up(a, bf16=False):
+        t = torch.from_numpy(np.ascontiguousarray(a))
+        return (t.view(torch.int16).view(torch.bfloat16) if bf16 else t).to(dev)
+
+    layer = MoELayer(shape, device=dev, fused=True)
+    fp8 = cfg.wdt == "fp8"
+    layer.set_weights(up(wl.w["w13"], cfg.wdt == "bf16"), up(wl.w["w2"], cfg.wdt == "bf16"),
+                      up(wl.w["w13_scales"]) if fp8 else None, up(wl.w["w2_scales"]) if fp8 else None)
+    x = up(wl.x, cfg.act == "bf16")
+    ids = up(wl.ids)
+    w = up(wl.weights)
+    torch.cuda.synchronize()
+
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    stages = ["layout", "permute", "gemm_w13", "gemm_w2", "combine"]
+    fns = [lambda: layer.layout(ids), lambda: layer.permute(x), layer.gemm_w13, layer.gemm_w2,
+           lambda: layer.combine(w)]
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        for f in fns:
+            f()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(args.steps)]
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        ev[s][0].record(stream)
+        for i, f in enumerate(fns):
+            f()
+            ev[s][i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = np.array([[ev[s][i].elapsed_time(ev[s][i + 1]) for i in range(len(stages))]
+                    for s in range(args.steps)])                      # ms
+    step_ms = wall * 1e3 / args.steps                 # whole-job clock, host included
+    gpu_ms = float(np.median(per.sum(axis=1)))        # sum of stage events, median step
+    st = layer.dev_status.cpu().numpy()
+    if st[0] != 0:
+        raise RuntimeError(f"dispatch layout flagged {st}")
+
+    counts = layer.counts.cpu().numpy()
+    work = algorithmic_work(cfg, counts)
+    stage_us = {k: float(np.median(per[:, i]) * 1e3) for i, k in enumerate(stages)}
+    gemm_us = stage_us["gemm_w13"] + stage_us["gemm_w2"]
+    peak_tf = MFMA_PEAK_TFLOPS[cfg.wdt]
+    gemm_tflops = work["gemm_flops"] / (gemm_us * 1e-6) / 1e12
+
+    # dominant kernel: the gate/up GEMM (two thirds of the FLOPs)
+    w13_us = float(np.mean(per[:, 2]) * 1e3)
+    t_hbm = work["w13_bytes"] / (HBM_PEAK_GBS * 1e9)
+    t_mfma = work["w13_flops"] / (peak_tf * 1e12)
+    if t_hbm >= t_mfma:
+        ach = work["w13_bytes"] / (w13_us * 1e-6) / 1e9
+        roof = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    else:
+        ach = work["w13_flops"] / (w13_us * 1e-6) / 1e12
+        roof = {"bound": "mfma", "achieved": ach, "peak": peak_tf, "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    roof["kernel"] = "grouped_gemm_kernel (moe_grouped_gemm_w13, fused SiLU*up, FP8 Z)"
+    roof["avg_us"] = w13_us
+    roof["algorithmic_bytes"] = work["w13_bytes"]
+    roof["algorithmic_flops"] = work["w13_flops"]
+    roof["mfma_frac"] = work["w13_flops"] / (w13_us * 1e-6) / 1e12 / peak_tf
+
+    out = {
+        "metric": METRIC,
+        "value": work["rows"] / (step_ms * 1e-3),
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": step_ms,
+        "gpu_ms_per_step": gpu_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.wdt,
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "T": cfg.T, "K": cfg.K, "E": cfg.E, "L": cfg.L,
+                   "H": cfg.H, "I": cfg.I, "R": cfg.R, "rows": work["rows"],
+                   "act": cfg.act, "weights": cfg.wdt, "seed": cfg.seed},
+        "gemm_tflops": gemm_tflops,
+        "gemm_mfma_frac": gemm_tflops / peak_tf,
+        "stage_us": stage_us,
+        "stage_gbs": {
+            "permute": None, "combine": None,
+        },
+        "roofline": roof,
+        "cpu_baseline": None,
+    }
+    # permute / combine algorithmic bandwidth
+    slot = layer.slot_of.cpu().numpy()
+    tok_local = int((slot >= 0).any(axis=1).sum())
+    xb = {"bf16": 2, "f32": 4}[cfg.act]
+    ab = {"fp8": 1, "bf16": 2, "f32": 4}[cfg.buf_dt]
+    ob = {"bf16": 2, "f32": 4}[cfg.out_dt]
+    perm_bytes = tok_local * cfg.H * xb + work["rows"] * cfg.H * ab + \
+        (work["rows"] * (cfg.H // 128) * 4 if cfg.buf_dt == "fp8" else 0) + cfg.T * cfg.K * 4
+    comb_bytes = work["rows"] * cfg.H * ob + cfg.T * cfg.H * ob + cfg.T * cfg.K * 8
+    out["stage_gbs"] = {"permute": perm_bytes / (stage_us["permute"] * 1e-6) / 1e9,
+                        "combine": comb_bytes / (stage_us["combine"] * 1e-6) / 1e9}
+
+    if not args.skip_cpu_baseline:
+        print("[bench] cpu baseline (oracle sample)", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_sample_tokens)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

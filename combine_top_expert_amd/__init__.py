@@ -1,0 +1,174 @@
+"""Python binding of libmoe_ep.so -- the MI355X (gfx950) MoE hot path.
+
+Argument marshalling only: every function below checks tensor placement,
+dtype and contiguity, derives sizes from shapes, and calls the C entry point
+of the same name in ``include/moe_ep.h`` on torch's current HIP stream.
+All computation happens in the library's HIP kernels; there is no CPU or
+PyTorch fallback.  Importing this package fails loudly if the library has
+not been built (``python -m combine_top_expert_amd.build``).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from pathlib import Path
+
+import torch
+
+__all__ = [
+    "MoEError", "LIB_PATH", "lib", "MOE_F32", "MOE_BF16", "MOE_FP8_E4M3",
+    "MOE_EPI_STORE_G", "MOE_EPI_SILU_MUL", "MOE_FLAG_CAPACITY", "MOE_FLAG_BAD_EXPERT_ID",
+    "moe_status_string", "moe_abi_version", "moe_dispatch_layout_workspace_bytes",
+    "moe_dispatch_layout", "moe_permute", "moe_grouped_gemm_w13", "moe_silu_mul",
+    "moe_grouped_gemm_w2", "moe_combine", "dtype_code",
+]
+
+LIB_PATH = Path(os.environ.get("MOE_EP_LIB", Path(__file__).resolve().parent / "libmoe_ep.so"))
+
+MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
+MOE_EPI_STORE_G, MOE_EPI_SILU_MUL = 0, 1
+MOE_FLAG_CAPACITY, MOE_FLAG_BAD_EXPERT_ID = 1, 2
+
+if not LIB_PATH.exists():
+    raise ImportError(f"{LIB_PATH} is not built; run `python -m combine_top_expert_amd.build` "
+                      "(the MoE path has no fallback without its HIP library)")
+lib = ctypes.CDLL(str(LIB_PATH))
+
+_p, _i, _i64, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
+_SIG = {
+    "moe_status_string": (ctypes.c_char_p, [_i]),
+    "moe_abi_version": (_i, []),
+    "moe_dispatch_layout_workspace_bytes": (_sz, [_i, _i, _i]),
+    "moe_dispatch_layout": (_i, [_p, _i, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _sz, _p]),
+    "moe_permute": (_i, [_p, _i, _i, _i, _i, _p, _i64, _p, _i, _p, _p]),
+    "moe_grouped_gemm_w13": (_i, [_p, _i, _p, _p, _i, _p, _p, _p, _i, _i64, _i, _i, _i, _p, _i, _p, _p]),
+    "moe_silu_mul": (_i, [_p, _p, _p, _i, _i64, _i, _p, _i, _p, _p]),
+    "moe_grouped_gemm_w2": (_i, [_p, _i, _p, _p, _i, _p, _p, _p, _i, _i64, _i, _i, _p, _i, _p]),
+    "moe_combine": (_i, [_p, _i, _p, _p, _i, _i, _i, _i64, _p, _i, _p]),
+}
+for _name, (_res, _args) in _SIG.items():
+    _f = getattr(lib, _name)
+    _f.restype, _f.argtypes = _res, _args
+
+
+class MoEError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed: {moe_status_string(status)} ({status})")
+        self.status = status
+
+
+def moe_status_string(status: int) -> str:
+    return lib.moe_status_string(int(status)).decode()
+
+
+def moe_abi_version() -> int:
+    return int(lib.moe_abi_version())
+
+
+def moe_dispatch_layout_workspace_bytes(T: int, K: int, L: int) -> int:
+    return int(lib.moe_dispatch_layout_workspace_bytes(T, K, L))
+
+
+# ---------------------------------------------------------------- marshalling helpers
+
+def dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return MOE_F32
+    if t.dtype == torch.bfloat16:
+        return MOE_BF16
+    if t.dtype in (torch.float8_e4m3fn, torch.uint8):
+        return MOE_FP8_E4M3
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t: torch.Tensor | None, name: str) -> int | None:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _i32(t: torch.Tensor | None, name: str) -> int | None:
+    if t is not None and t.dtype != torch.int32:
+        raise TypeError(f"{name} must be int32")
+    return _ptr(t, name)
+
+
+def _f32(t: torch.Tensor | None, name: str) -> int | None:
+    if t is not None and t.dtype != torch.float32:
+        raise TypeError(f"{name} must be float32")
+    return _ptr(t, name)
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise MoEError(fn, status)
+
+
+# ---------------------------------------------------------------- entry points
+
+def moe_dispatch_layout(topk_ids, E_global, expert_begin, L, R, BM, counts, offsets, slot_of,
+                        row_src, tile_offsets, dev_status, workspace) -> None:
+    """topk_ids [T,K] int32 -> counts [L], offsets [L+1], slot_of [T,K],
+    row_src [rows_cap], tile_offsets [L+1], dev_status [2] (all int32)."""
+    T, K = topk_ids.shape
+    _check("moe_dispatch_layout", lib.moe_dispatch_layout(
+        _i32(topk_ids, "topk_ids"), T, K, E_global, expert_begin, L, R, BM,
+        _i32(counts, "counts"), _i32(offsets, "offsets"), _i32(slot_of, "slot_of"),
+        _i32(row_src, "row_src"), _i32(tile_offsets, "tile_offsets"),
+        _i32(dev_status, "dev_status"), _ptr(workspace, "workspace"),
+        workspace.numel() * workspace.element_size(), _stream(topk_ids)))
+
+
+def moe_permute(x, slot_of, buf, buf_scales=None) -> None:
+    """x [T,H] (fp32|bf16), slot_of [T,K] -> buf [rows_cap,H] (+ scales for FP8)."""
+    T, H = x.shape
+    K = slot_of.shape[1]
+    _check("moe_permute", lib.moe_permute(
+        _ptr(x, "x"), dtype_code(x), T, K, H, _i32(slot_of, "slot_of"), buf.shape[0],
+        _ptr(buf, "buf"), dtype_code(buf), _f32(buf_scales, "buf_scales"), _stream(x)))
+
+
+def moe_grouped_gemm_w13(a, a_scales, w13, w13_scales, counts, offsets, epi, out,
+                         out_scales=None) -> None:
+    """a [rows_cap,H], w13 [L,2I,H] -> G [rows_cap,2I] fp32 or Z [rows_cap,I]."""
+    L, N, H = w13.shape
+    _check("moe_grouped_gemm_w13", lib.moe_grouped_gemm_w13(
+        _ptr(a, "a"), dtype_code(a), _f32(a_scales, "a_scales"), _ptr(w13, "w13"),
+        dtype_code(w13), _f32(w13_scales, "w13_scales"), _i32(counts, "counts"),
+        _i32(offsets, "offsets"), L, a.shape[0], H, N // 2, int(epi), _ptr(out, "out"),
+        dtype_code(out), _f32(out_scales, "out_scales"), _stream(a)))
+
+
+def moe_silu_mul(g, counts, offsets, z, z_scales=None) -> None:
+    """g [rows_cap,2I] fp32 -> z [rows_cap,I] (fp32|bf16|FP8 + scales)."""
+    rows_cap, N = g.shape
+    _check("moe_silu_mul", lib.moe_silu_mul(
+        _f32(g, "g"), _i32(counts, "counts"), _i32(offsets, "offsets"), counts.shape[0],
+        rows_cap, N // 2, _ptr(z, "z"), dtype_code(z), _f32(z_scales, "z_scales"), _stream(g)))
+
+
+def moe_grouped_gemm_w2(z, z_scales, w2, w2_scales, counts, offsets, out) -> None:
+    """z [rows_cap,I], w2 [L,H,I] -> out [rows_cap,H] (fp32|bf16)."""
+    L, H, I = w2.shape
+    _check("moe_grouped_gemm_w2", lib.moe_grouped_gemm_w2(
+        _ptr(z, "z"), dtype_code(z), _f32(z_scales, "z_scales"), _ptr(w2, "w2"), dtype_code(w2),
+        _f32(w2_scales, "w2_scales"), _i32(counts, "counts"), _i32(offsets, "offsets"), L,
+        z.shape[0], H, I, _ptr(out, "out"), dtype_code(out), _stream(z)))
+
+
+def moe_combine(expert_out, slot_of, topk_weights, y) -> None:
+    """expert_out [rows_cap,H], slot_of [T,K], topk_weights [T,K] -> y [T,H]."""
+    T, K = slot_of.shape
+    H = y.shape[1]
+    _check("moe_combine", lib.moe_combine(
+        _ptr(expert_out, "expert_out"), dtype_code(expert_out), _i32(slot_of, "slot_of"),
+        _f32(topk_weights, "topk_weights"), T, K, H, expert_out.shape[0], _ptr(y, "y"),
+        dtype_code(y), _stream(y)))

@@ -1,0 +1,345 @@
+// moe_dispatch_layout: per-expert counts, offsets, (t,k) -> row slots and
+// the row -> (t,k) reverse map, deterministic and atomics-free in global
+// memory.
+//
+// Semantics ("SGLang、NCCL 与 MoE EP" §2.3.4 and §2.3.6; "DeepEP 架构与实现笔记"
+// §9.4 dispatch_convert): routes are numbered i = t*K + k; expert e's rows
+// are handed out in increasing i, starting at offsets[e].  The page's
+// per-expert atomic counter gives an arrival-order permutation of the same
+// rows; ordering by i instead makes the layout unique.
+//
+// Three launches:
+//   1. count : every block takes PAIRS_PER_BLOCK consecutive routes and
+//              histograms them per local expert in LDS -> ws_hist[blk][L].
+//   2. scan  : one block turns the histograms into exclusive prefixes over
+//              blocks (ws_hist in place), totals -> counts, offsets,
+//              tile_offsets, dev_status.
+//   3. place : every block re-reads its routes; inside each 64-route
+//              wavefront chunk the rank of a route among equal experts comes
+//              from ballot + mbcnt; chunk ranks are scanned in LDS and added
+//              to the block prefix.  Writes slot_of and row_src, and marks
+//              padding rows of row_src with -1.
+
+#include "moe_common.h"
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / MOE_WAVE;            // 4
+constexpr int kChunksPerBlock = 16;                    // 64-route chunks
+constexpr int kPairsPerBlock = kChunksPerBlock * MOE_WAVE;  // 1024
+constexpr int kScanThreads = 1024;
+constexpr int kMaxL = 1024;
+
+struct LayoutArgs {
+  const int32_t* ids;
+  int64_t n_pairs;   // T*K
+  int E_global, expert_begin, L, R, BM;
+  int64_t rows_cap;
+  int n_blocks;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* slot_of;
+  int32_t* row_src;
+  int32_t* tile_offsets;
+  int32_t* dev_status;
+  int32_t* ws_hist;    // [n_blocks][L]
+  int32_t* ws_bad;     // [n_blocks]
+};
+
+// local expert of a route, -1 if none; *bad set for ids outside [-1, E)
+__device__ __forceinline__ int local_expert(const LayoutArgs& a, int64_t p, bool* bad) {
+  if (p >= a.n_pairs) return -1;
+  int g = a.ids[p];
+  if (g < -1 || g >= a.E_global) { *bad = true; return -1; }
+  int e = g - a.expert_begin;
+  return (g >= 0 && e >= 0 && e < a.L) ? e : -1;
+}
+
+__global__ __launch_bounds__(kThreads) void layout_count_kernel(LayoutArgs a) {
+  __shared__ int hist[kMaxL];
+  __shared__ int any_bad;
+  for (int e = threadIdx.x; e < a.L; e += kThreads) hist[e] = 0;
+  if (threadIdx.x == 0) any_bad = 0;
+  __syncthreads();
+  const int64_t base = static_cast<int64_t>(blockIdx.x) * kPairsPerBlock;
+  bool bad = false;
+  for (int i = threadIdx.x; i < kPairsPerBlock; i += kThreads) {
+    int e = local_expert(a, base + i, &bad);
+    if (e >= 0) atomicAdd(&hist[e], 1);
+  }
+  if (bad) any_bad = 1;
+  __syncthreads();
+  int32_t* out = a.ws_hist + static_cast<int64_t>(blockIdx.x) * a.L;
+  for (int e = threadIdx.x; e < a.L; e += kThreads) out[e] = hist[e];
+  if (threadIdx.x == 0) a.ws_bad[blockIdx.x] = any_bad;
+}
+
+// inclusive scan over v[0..n) in LDS by a 1024-thread block (Hillis-Steele)
+__device__ void block_inclusive_scan(int* v, int* tmp, int n) {
+  for (int d = 1; d < n; d <<= 1) {
+    int t = threadIdx.x;
+    int x = 0;
+    if (t < n) x = v[t] + (t >= d ? v[t - d] : 0);
+    __syncthreads();
+    if (t < n) tmp[t] = x;
+    __syncthreads();
+    if (t < n) v[t] = tmp[t];
+    __syncthreads();
+  }
+}
+
+__global__ __launch_bounds__(kScanThreads) void layout_scan_kernel(LayoutArgs a) {
+  constexpr int kTileInts = 8192;
+  __shared__ int tile[kTileInts];
+  __shared__ int vals[kMaxL];
+  __shared__ int tmp[kMaxL];
+  __shared__ int flags, dropped;
+  const int L = a.L;
+  const int e = threadIdx.x;
+  if (threadIdx.x == 0) { flags = 0; dropped = 0; }
+  // 1. exclusive prefix over blocks, a tile of rows at a time
+  const int rows_per_tile = kTileInts / L;
+  int running = 0;
+  for (int b0 = 0; b0 < a.n_blocks; b0 += rows_per_tile) {
+    const int nb = min(rows_per_tile, a.n_blocks - b0);
+    const int n = nb * L;
+    const int32_t* src = a.ws_hist + static_cast<int64_t>(b0) * L;
+    __syncthreads();
+    for (int i = threadIdx.x; i < n; i += kScanThreads) tile[i] = src[i];
+    __syncthreads();
+    if (e < L) {
+      for (int b = 0; b < nb; ++b) {
+        int v = tile[b * L + e];
+        tile[b * L + e] = running;
+        running += v;
+      }
+    }
+    __syncthreads();
+    int32_t* dst = a.ws_hist + static_cast<int64_t>(b0) * L;
+    for (int i = threadIdx.x; i < n; i += kScanThreads) dst[i] = tile[i];
+  }
+  __syncthreads();
+  // 2. flags from the count pass
+  int bad = 0;
+  for (int b = threadIdx.x; b < a.n_blocks; b += kScanThreads) bad |= a.ws_bad[b];
+  if (bad) atomicOr(&flags, MOE_FLAG_BAD_EXPERT_ID);
+  // 3. counts, capacity check
+  int cnt = 0;
+  if (e < L) {
+    cnt = running;
+    if (a.R > 0 && running > a.R) {
+      cnt = a.R;
+      atomicOr(&flags, MOE_FLAG_CAPACITY);
+      atomicAdd(&dropped, running - a.R);
+    }
+    a.counts[e] = cnt;
+    vals[e] = cnt;
+  }
+  __syncthreads();
+  // 4. offsets
+  if (a.R > 0) {
+    if (e <= L) a.offsets[e] = e * a.R;
+  } else {
+    block_inclusive_scan(vals, tmp, L);
+    if (e < L) a.offsets[e + 1] = vals[e];
+    if (e == 0) a.offsets[0] = 0;
+  }
+  __syncthreads();
+  // 5. tile offsets
+  if (e < L) vals[e] = (cnt + a.BM - 1) / a.BM;
+  __syncthreads();
+  block_inclusive_scan(vals, tmp, L);
+  if (e < L) a.tile_offsets[e + 1] = vals[e];
+  if (e == 0) a.tile_offsets[0] = 0;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    a.dev_status[0] = flags;
+    a.dev_status[1] = dropped;
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void layout_place_kernel(LayoutArgs a) {
+  __shared__ int chunk_cnt[kChunksPerBlock][64];  // per chunk, per expert (L <= 64 path)
+  __shared__ int base[kMaxL];
+  const int L = a.L;
+  const int wave = threadIdx.x / MOE_WAVE;
+  const int lane = moe::lane_id();
+  const int blk = blockIdx.x;
+
+  if (blk < a.n_blocks) {
+    const int32_t* pre = a.ws_hist + static_cast<int64_t>(blk) * L;
+    for (int e = threadIdx.x; e < L; e += kThreads) base[e] = pre[e];
+    const int64_t pbase = static_cast<int64_t>(blk) * kPairsPerBlock;
+
+    // Per-chunk rank among equal experts.  For L <= 64 the per-chunk counts
+    // live in LDS and one scan over chunks follows; for larger L the block's
+    // chunks are processed in order with a running per-expert counter.
+    int e_of[kChunksPerBlock / kWaves];
+    int rank[kChunksPerBlock / kWaves];
+    if (L <= 64) {
+      for (int i = threadIdx.x; i < kChunksPerBlock * 64; i += kThreads)
+        (&chunk_cnt[0][0])[i] = 0;
+      __syncthreads();
+      for (int r = 0; r < kChunksPerBlock / kWaves; ++r) {
+        const int c = r * kWaves + wave;
+        bool bad = false;
+        const int e = local_expert(a, pbase + c * MOE_WAVE + lane, &bad);
+        uint64_t left = moe::ballot(e >= 0);
+        int my_rank = 0;
+        while (left) {
+          const int leader = __builtin_ctzll(left);
+          const int le = __builtin_amdgcn_readlane(e, leader);
+          const uint64_t m = moe::ballot(e == le);
+          if (e == le) {
+            my_rank = moe::mbcnt(m);
+            if (lane == leader) chunk_cnt[c][le] = __builtin_popcountll(m);
+          }
+          left &= ~m;
+        }
+        e_of[r] = e;
+        rank[r] = my_rank;
+      }
+      __syncthreads();
+      // exclusive scan over the block's chunks, per expert
+      for (int e = threadIdx.x; e < L; e += kThreads) {
+        int run = 0;
+        for (int c = 0; c < kChunksPerBlock; ++c) {
+          int v = chunk_cnt[c][e];
+          chunk_cnt[c][e] = run;
+          run += v;
+        }
+      }
+      __syncthreads();
+      for (int r = 0; r < kChunksPerBlock / kWaves; ++r) {
+        const int c = r * kWaves + wave;
+        const int64_t p = pbase + c * MOE_WAVE + lane;
+        if (p >= a.n_pairs) continue;
+        const int e = e_of[r];
+        int slot = -1;
+        if (e >= 0) {
+          const int s = base[e] + chunk_cnt[c][e] + rank[r];
+          if (a.R <= 0 || s < a.R) {
+            const int q = a.offsets[e] + s;
+            if (q < a.rows_cap) {
+              slot = q;
+              a.row_src[q] = static_cast<int32_t>(p);
+            }
+          }
+        }
+        a.slot_of[p] = slot;
+      }
+    } else {
+      // L > 64: chunks in order; each chunk's leaders bump the running count
+      // in base[] after every lane of that chunk has read it.
+      __syncthreads();
+      for (int c = 0; c < kChunksPerBlock; ++c) {
+        const int64_t p = pbase + c * MOE_WAVE + lane;
+        int e = -1;
+        int my_rank = 0;
+        uint64_t mask_of_mine = 0;
+        if (wave == 0) {
+          bool bad = false;
+          e = local_expert(a, p, &bad);
+          uint64_t left = moe::ballot(e >= 0);
+          while (left) {
+            const int leader = __builtin_ctzll(left);
+            const int le = __builtin_amdgcn_readlane(e, leader);
+            const uint64_t m = moe::ballot(e == le);
+            if (e == le) { my_rank = moe::mbcnt(m); mask_of_mine = m; }
+            left &= ~m;
+          }
+          int slot = -1;
+          if (e >= 0) {
+            const int s = base[e] + my_rank;
+            if (a.R <= 0 || s < a.R) {
+              const int q = a.offsets[e] + s;
+              if (q < a.rows_cap) {
+                slot = q;
+                a.row_src[q] = static_cast<int32_t>(p);
+              }
+            }
+          }
+          if (p < a.n_pairs) a.slot_of[p] = slot;
+        }
+        __syncthreads();
+        if (wave == 0 && e >= 0 && moe::mbcnt(mask_of_mine) == 0)
+          base[e] += __builtin_popcountll(mask_of_mine);
+        __syncthreads();
+      }
+    }
+  }
+
+  // padding rows of row_src -> -1 (valid rows are written above)
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
+  for (int64_t q = static_cast<int64_t>(blk) * kThreads + threadIdx.x; q < a.rows_cap; q += stride) {
+    bool pad;
+    if (a.R > 0) {
+      const int e = static_cast<int>(q / a.R);
+      pad = (q - static_cast<int64_t>(e) * a.R) >= a.counts[e];
+    } else {
+      pad = q >= a.offsets[L];
+    }
+    if (pad) a.row_src[q] = -1;
+  }
+}
+
+}  // namespace
+
+extern "C" size_t moe_dispatch_layout_workspace_bytes(int T, int K, int L) {
+  if (T < 0 || K < 0 || L <= 0) return 0;
+  const int64_t pairs = static_cast<int64_t>(T) * K;
+  const int64_t nblk = (pairs + kPairsPerBlock - 1) / kPairsPerBlock;
+  return static_cast<size_t>((nblk * L + nblk + 64) * sizeof(int32_t));
+}
+
+extern "C" moe_status moe_dispatch_layout(const int32_t* topk_ids, int T, int K, int E_global,
+                                          int expert_begin, int L, int R, int BM,
+                                          int32_t* counts, int32_t* offsets, int32_t* slot_of,
+                                          int32_t* row_src, int32_t* tile_offsets,
+                                          int32_t* dev_status, void* workspace,
+                                          size_t workspace_bytes, hipStream_t stream) {
+  MOE_CHECK(T >= 0 && K > 0 && E_global > 0 && L >= 1 && L <= kMaxL && R >= 0 && BM > 0 &&
+                expert_begin >= 0 && expert_begin + L <= E_global,
+            MOE_ERR_INVALID_ARG);
+  const int64_t pairs = static_cast<int64_t>(T) * K;
+  MOE_CHECK(pairs <= (int64_t(1) << 30), MOE_ERR_UNSUPPORTED);
+  const int64_t rows_cap = R > 0 ? static_cast<int64_t>(L) * R : pairs;
+  MOE_CHECK(rows_cap <= (int64_t(1) << 31) - 1, MOE_ERR_UNSUPPORTED);
+  MOE_CHECK(counts && offsets && tile_offsets && dev_status && workspace, MOE_ERR_INVALID_ARG);
+  MOE_CHECK(pairs == 0 || (topk_ids && slot_of), MOE_ERR_INVALID_ARG);
+  MOE_CHECK(rows_cap == 0 || row_src, MOE_ERR_INVALID_ARG);
+  MOE_CHECK(workspace_bytes >= moe_dispatch_layout_workspace_bytes(T, K, L), MOE_ERR_WORKSPACE);
+
+  LayoutArgs a{};
+  a.ids = topk_ids;
+  a.n_pairs = pairs;
+  a.E_global = E_global;
+  a.expert_begin = expert_begin;
+  a.L = L;
+  a.R = R;
+  a.BM = BM;
+  a.rows_cap = rows_cap;
+  a.n_blocks = static_cast<int>((pairs + kPairsPerBlock - 1) / kPairsPerBlock);
+  a.counts = counts;
+  a.offsets = offsets;
+  a.slot_of = slot_of;
+  a.row_src = row_src;
+  a.tile_offsets = tile_offsets;
+  a.dev_status = dev_status;
+  a.ws_hist = static_cast<int32_t*>(workspace);
+  a.ws_bad = a.ws_hist + static_cast<int64_t>(a.n_blocks) * L;
+
+  if (a.n_blocks > 0) {
+    layout_count_kernel<<<a.n_blocks, kThreads, 0, stream>>>(a);
+    MOE_LAUNCH_CHECK();
+  }
+  layout_scan_kernel<<<1, kScanThreads, 0, stream>>>(a);
+  MOE_LAUNCH_CHECK();
+  // at least enough blocks to sweep row_src's padding in a few passes
+  const int64_t fill_blocks = (rows_cap + kThreads * 8 - 1) / (kThreads * 8);
+  const int grid = static_cast<int>(std::max<int64_t>(std::max<int64_t>(a.n_blocks, fill_blocks), 1));
+  layout_place_kernel<<<grid, kThreads, 0, stream>>>(a);
+  MOE_LAUNCH_CHECK();
+  return MOE_OK;
+}

@@ -1,0 +1,201 @@
+// moe_silu_mul and moe_combine.
+//
+// silu_mul: Z = SiLU(gate) * up on the valid rows of an expert-major fp32
+// G buffer ("SGLang Expert Compute Backend" §3.6: non-interleaved gate/up,
+// activation applied to valid expert rows only, Z re-quantised with its own
+// per-128 scales before the down GEMM).  One wavefront per row; a
+// 128-column Z group spans 32 lanes x 4 values.
+//
+// combine: y[t] = sum_k w[t,k] * out[slot_of[t,k]] ("SGLang、NCCL 与 MoE EP"
+// §1.1 and §2.3.6; "DeepEP 架构与实现笔记" §9.4 combine_convert).  One
+// wavefront per token; every lane owns 8 consecutive columns per step and
+// has all K source rows of that step in flight at once.  Products and sums
+// are separate fp32 operations in k order (no fused multiply-add), so the
+// result equals a plain fp32 evaluation of the sum term by term.
+
+#include "moe_common.h"
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kRowsPerBlock = kThreads / MOE_WAVE;
+
+// expert of row q, or -1 if q is a padding row
+__device__ __forceinline__ bool valid_row(const int32_t* counts, const int32_t* offsets, int L,
+                                          int64_t q) {
+  int lo = 0, hi = L;          // largest e with offsets[e] <= q
+  if (q < offsets[0]) return false;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (offsets[mid] <= q) lo = mid; else hi = mid;
+  }
+  return q < static_cast<int64_t>(offsets[lo]) + counts[lo];
+}
+
+template <int ZDT>  // 0 f32, 1 bf16, 2 fp8
+__global__ __launch_bounds__(kThreads) void silu_mul_kernel(const float* __restrict__ g,
+                                                            const int32_t* __restrict__ counts,
+                                                            const int32_t* __restrict__ offsets,
+                                                            int L, int64_t rows_cap, int I,
+                                                            uint8_t* __restrict__ z,
+                                                            float* __restrict__ zs) {
+  const int lane = moe::lane_id();
+  const int64_t q = static_cast<int64_t>(blockIdx.x) * kRowsPerBlock + (threadIdx.x >> 6);
+  if (q >= rows_cap || !valid_row(counts, offsets, L, q)) return;
+  const float4* grow = reinterpret_cast<const float4*>(g + q * 2 * I);
+  const int nchunk = I / 4;                       // 4 columns per lane-step
+  for (int c0 = 0; c0 < nchunk; c0 += MOE_WAVE) {
+    const int c = c0 + lane;
+    const bool live = c < nchunk;                 // nchunk % 32 == 0: groups stay whole
+    float4 gt = make_float4(0.f, 0.f, 0.f, 0.f), up = gt;
+    if (live) {
+      gt = grow[c];
+      up = grow[nchunk + c];
+    }
+    const float v[4] = {moe::silu(gt.x) * up.x, moe::silu(gt.y) * up.y, moe::silu(gt.z) * up.z,
+                        moe::silu(gt.w) * up.w};
+    if constexpr (ZDT == 2) {
+      float m = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+      m = moe::group16_max(m);
+      m = fmaxf(m, __shfl_xor(m, 16));
+      const float amax = moe::fp8_group_amax_clamp(m);
+      const float inv = moe::fp8_group_inv(amax);
+      if (live) {
+        reinterpret_cast<uint32_t*>(z + q * I)[c] =
+            moe::f32x4_to_e4m3(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
+        if ((lane & 31) == 0) zs[q * (I / 128) + c / 32] = moe::fp8_group_scale(amax);
+      }
+    } else if constexpr (ZDT == 1) {
+      if (live) {
+        const uint32_t lo = moe::f32_to_bf16(v[0]) | (uint32_t(moe::f32_to_bf16(v[1])) << 16);
+        const uint32_t hi = moe::f32_to_bf16(v[2]) | (uint32_t(moe::f32_to_bf16(v[3])) << 16);
+        reinterpret_cast<uint2*>(z + q * I * 2)[c] = make_uint2(lo, hi);
+      }
+    } else {
+      if (live) reinterpret_cast<float4*>(z + q * I * 4)[c] = make_float4(v[0], v[1], v[2], v[3]);
+    }
+  }
+}
+
+constexpr int kMaxK = 64;
+constexpr int kKU = 8;          // source rows in flight per lane
+
+template <bool kInBf16, bool kOutBf16>
+__global__ __launch_bounds__(kThreads) void combine_kernel(const uint8_t* __restrict__ eo,
+                                                           const int32_t* __restrict__ slot_of,
+                                                           const float* __restrict__ w, int T,
+                                                           int K, int H, int64_t rows_cap,
+                                                           uint8_t* __restrict__ y) {
+  const int lane = moe::lane_id();
+  const int t = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+  if (t >= T) return;
+  constexpr int IB = kInBf16 ? 2 : 4;
+  constexpr int OB = kOutBf16 ? 2 : 4;
+  const int32_t* so = slot_of + static_cast<int64_t>(t) * K;
+  const float* wt = w + static_cast<int64_t>(t) * K;
+  const int nchunk = H / 8;
+  for (int c = lane; c < nchunk; c += MOE_WAVE) {
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int k0 = 0; k0 < K; k0 += kKU) {
+      uint4 raw[kKU][IB == 2 ? 1 : 2];
+      bool ok[kKU];
+#pragma unroll
+      for (int u = 0; u < kKU; ++u) {
+        const int k = k0 + u;
+        const int s = k < K ? so[k] : -1;
+        ok[u] = s >= 0 && s < rows_cap;
+        const uint4* row = reinterpret_cast<const uint4*>(eo + static_cast<int64_t>(ok[u] ? s : 0) * H * IB +
+                                                          static_cast<int64_t>(c) * 8 * IB);
+#pragma unroll
+        for (int v = 0; v < (IB == 2 ? 1 : 2); ++v)
+          raw[u][v] = ok[u] ? row[v] : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int u = 0; u < kKU; ++u) {
+        if (!ok[u]) continue;
+        const float wk = wt[k0 + u];
+        float v[8];
+        if constexpr (kInBf16) {
+          const uint32_t ww[4] = {raw[u][0].x, raw[u][0].y, raw[u][0].z, raw[u][0].w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            v[2 * i] = __uint_as_float(ww[i] << 16);
+            v[2 * i + 1] = __uint_as_float(ww[i] & 0xffff0000u);
+          }
+        } else {
+          const uint32_t ww[8] = {raw[u][0].x, raw[u][0].y, raw[u][0].z, raw[u][0].w,
+                                  raw[u][1].x, raw[u][1].y, raw[u][1].z, raw[u][1].w};
+#pragma unroll
+          for (int i = 0; i < 8; ++i) v[i] = __uint_as_float(ww[i]);
+        }
+        {
+          // product and sum rounded separately, in k order (no FMA contraction)
+#pragma clang fp contract(off)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc[i] = acc[i] + wk * v[i];
+        }
+      }
+    }
+    uint8_t* dst = y + static_cast<int64_t>(t) * H * OB + static_cast<int64_t>(c) * 8 * OB;
+    if constexpr (kOutBf16) {
+      uint4 o;
+      o.x = moe::f32_to_bf16(acc[0]) | (uint32_t(moe::f32_to_bf16(acc[1])) << 16);
+      o.y = moe::f32_to_bf16(acc[2]) | (uint32_t(moe::f32_to_bf16(acc[3])) << 16);
+      o.z = moe::f32_to_bf16(acc[4]) | (uint32_t(moe::f32_to_bf16(acc[5])) << 16);
+      o.w = moe::f32_to_bf16(acc[6]) | (uint32_t(moe::f32_to_bf16(acc[7])) << 16);
+      moe::store_nt16(dst, o);
+    } else {
+      reinterpret_cast<float4*>(dst)[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+      reinterpret_cast<float4*>(dst)[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+    }
+  }
+}
+
+}  // namespace
+
+extern "C" moe_status moe_silu_mul(const float* g, const int32_t* counts, const int32_t* offsets,
+                                   int L, int64_t rows_cap, int I, void* z, moe_dtype z_dt,
+                                   float* z_scales, hipStream_t stream) {
+  MOE_CHECK(L >= 1 && rows_cap >= 0 && I > 0, MOE_ERR_INVALID_ARG);
+  MOE_CHECK(moe_host::valid_dtype(z_dt), MOE_ERR_INVALID_ARG);
+  MOE_CHECK(I % 128 == 0, MOE_ERR_UNSUPPORTED);
+  if (rows_cap == 0) return MOE_OK;
+  MOE_CHECK(g && counts && offsets && z, MOE_ERR_INVALID_ARG);
+  MOE_CHECK(z_dt != MOE_FP8_E4M3 || z_scales, MOE_ERR_INVALID_ARG);
+  const int64_t grid = (rows_cap + kRowsPerBlock - 1) / kRowsPerBlock;
+  MOE_CHECK(grid <= 0x7fffffff, MOE_ERR_UNSUPPORTED);
+  auto* zo = static_cast<uint8_t*>(z);
+  if (z_dt == MOE_F32)
+    silu_mul_kernel<0><<<grid, kThreads, 0, stream>>>(g, counts, offsets, L, rows_cap, I, zo, nullptr);
+  else if (z_dt == MOE_BF16)
+    silu_mul_kernel<1><<<grid, kThreads, 0, stream>>>(g, counts, offsets, L, rows_cap, I, zo, nullptr);
+  else
+    silu_mul_kernel<2><<<grid, kThreads, 0, stream>>>(g, counts, offsets, L, rows_cap, I, zo, z_scales);
+  MOE_LAUNCH_CHECK();
+  return MOE_OK;
+}
+
+extern "C" moe_status moe_combine(const void* expert_out, moe_dtype eo_dt, const int32_t* slot_of,
+                                  const float* topk_weights, int T, int K, int H, int64_t rows_cap,
+                                  void* y, moe_dtype y_dt, hipStream_t stream) {
+  MOE_CHECK(T >= 0 && K > 0 && H > 0 && rows_cap >= 0, MOE_ERR_INVALID_ARG);
+  MOE_CHECK(moe_host::valid_dtype(eo_dt) && moe_host::valid_dtype(y_dt), MOE_ERR_INVALID_ARG);
+  MOE_CHECK(eo_dt != MOE_FP8_E4M3 && y_dt != MOE_FP8_E4M3, MOE_ERR_UNSUPPORTED);
+  MOE_CHECK(H % 8 == 0 && K <= kMaxK, MOE_ERR_UNSUPPORTED);
+  if (T == 0) return MOE_OK;
+  MOE_CHECK(slot_of && topk_weights && y && (rows_cap == 0 || expert_out), MOE_ERR_INVALID_ARG);
+  const int grid = (T + kRowsPerBlock - 1) / kRowsPerBlock;
+  auto* eo = static_cast<const uint8_t*>(expert_out);
+  auto* yo = static_cast<uint8_t*>(y);
+  const bool ib = eo_dt == MOE_BF16, ob = y_dt == MOE_BF16;
+  if (ib && ob)
+    combine_kernel<true, true><<<grid, kThreads, 0, stream>>>(eo, slot_of, topk_weights, T, K, H, rows_cap, yo);
+  else if (ib)
+    combine_kernel<true, false><<<grid, kThreads, 0, stream>>>(eo, slot_of, topk_weights, T, K, H, rows_cap, yo);
+  else if (ob)
+    combine_kernel<false, true><<<grid, kThreads, 0, stream>>>(eo, slot_of, topk_weights, T, K, H, rows_cap, yo);
+  else
+    combine_kernel<false, false><<<grid, kThreads, 0, stream>>>(eo, slot_of, topk_weights, T, K, H, rows_cap, yo);
+  MOE_LAUNCH_CHECK();
+  return MOE_OK;
+}

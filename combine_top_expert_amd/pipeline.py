@@ -1,0 +1,123 @@
+"""One GPU's MoE layer: device buffers plus the six entry points in order.
+
+torch provides device memory and the stream; every step of the layer runs
+in libmoe_ep.so:
+
+    moe_dispatch_layout -> moe_permute -> moe_grouped_gemm_w13 (fused SiLU*up)
+      -> moe_grouped_gemm_w2 -> moe_combine
+
+or, unfused, moe_grouped_gemm_w13 (G) -> moe_silu_mul -> moe_grouped_gemm_w2.
+Buffers are sized from capacity bounds once, so a step never allocates and
+its launch shapes never depend on the routing.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import torch
+
+from . import (MOE_EPI_SILU_MUL, MOE_EPI_STORE_G, moe_combine, moe_dispatch_layout,
+               moe_dispatch_layout_workspace_bytes, moe_grouped_gemm_w2, moe_grouped_gemm_w13,
+               moe_permute, moe_silu_mul)
+
+_TORCH = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8}
+
+
+@dataclass(frozen=True)
+class LayerShape:
+    T: int
+    K: int
+    E: int              # global experts
+    expert_begin: int
+    L: int              # local experts
+    H: int
+    I: int
+    R: int              # capacity per local expert, 0 = exact-fit
+    act: str            # token activations: "f32" | "bf16"
+    wdt: str            # expert weights: "f32" | "bf16" | "fp8"
+    BM: int = 128
+
+    @property
+    def rows_cap(self) -> int:
+        return self.L * self.R if self.R > 0 else self.T * self.K
+
+    @property
+    def buf_dt(self) -> str:
+        return "fp8" if self.wdt == "fp8" else self.act
+
+    @property
+    def z_dt(self) -> str:
+        return "fp8" if self.wdt == "fp8" else ("f32" if self.wdt == "f32" else "bf16")
+
+    @property
+    def out_dt(self) -> str:
+        return "f32" if self.act == "f32" else "bf16"
+
+
+class MoELayer:
+    def __init__(self, shape: LayerShape, device="cuda", fused: bool = True):
+        s = self.shape = shape
+        self.fused = fused
+        dev = torch.device(device)
+        i32 = dict(dtype=torch.int32, device=dev)
+        rc = s.rows_cap
+        self.counts = torch.zeros(s.L, **i32)
+        self.offsets = torch.zeros(s.L + 1, **i32)
+        self.slot_of = torch.zeros(s.T, s.K, **i32)
+        self.row_src = torch.zeros(max(rc, 1), **i32)[:rc]
+        self.tile_offsets = torch.zeros(s.L + 1, **i32)
+        self.dev_status = torch.zeros(2, **i32)
+        ws = moe_dispatch_layout_workspace_bytes(s.T, s.K, s.L)
+        self.workspace = torch.zeros(max(ws, 4), dtype=torch.uint8, device=dev)
+        self.buf = torch.empty(rc, s.H, dtype=_TORCH[s.buf_dt], device=dev)
+        self.buf_scales = (torch.empty(rc, s.H // 128, dtype=torch.float32, device=dev)
+                           if s.buf_dt == "fp8" else None)
+        self.g = None if fused else torch.empty(rc, 2 * s.I, dtype=torch.float32, device=dev)
+        self.z = torch.empty(rc, s.I, dtype=_TORCH[s.z_dt], device=dev)
+        self.z_scales = (torch.empty(rc, s.I // 128, dtype=torch.float32, device=dev)
+                         if s.z_dt == "fp8" else None)
+        self.out = torch.empty(rc, s.H, dtype=_TORCH[s.out_dt], device=dev)
+        self.y = torch.empty(s.T, s.H, dtype=_TORCH[s.out_dt], device=dev)
+        self.w13 = self.w13_scales = self.w2 = self.w2_scales = None
+
+    def set_weights(self, w13, w2, w13_scales=None, w2_scales=None):
+        self.w13, self.w2, self.w13_scales, self.w2_scales = w13, w2, w13_scales, w2_scales
+
+    # ---- the six steps
+    def layout(self, topk_ids):
+        s = self.shape
+        moe_dispatch_layout(topk_ids, s.E, s.expert_begin, s.L, s.R, s.BM, self.counts,
+                            self.offsets, self.slot_of, self.row_src, self.tile_offsets,
+                            self.dev_status, self.workspace)
+
+    def permute(self, x):
+        moe_permute(x, self.slot_of, self.buf, self.buf_scales)
+
+    def gemm_w13(self):
+        if self.fused:
+            moe_grouped_gemm_w13(self.buf, self.buf_scales, self.w13, self.w13_scales, self.counts,
+                                 self.offsets, MOE_EPI_SILU_MUL, self.z, self.z_scales)
+        else:
+            moe_grouped_gemm_w13(self.buf, self.buf_scales, self.w13, self.w13_scales, self.counts,
+                                 self.offsets, MOE_EPI_STORE_G, self.g)
+
+    def silu_mul(self):
+        if not self.fused:
+            moe_silu_mul(self.g, self.counts, self.offsets, self.z, self.z_scales)
+
+    def gemm_w2(self):
+        moe_grouped_gemm_w2(self.z, self.z_scales, self.w2, self.w2_scales, self.counts,
+                            self.offsets, self.out)
+
+    def combine(self, topk_weights):
+        moe_combine(self.out, self.slot_of, topk_weights, self.y)
+
+    def forward(self, x, topk_ids, topk_weights):
+        """The whole path on the current stream; returns y [T,H] (no sync)."""
+        self.layout(topk_ids)
+        self.permute(x)
+        self.gemm_w13()
+        self.silu_mul()
+        self.gemm_w2()
+        self.combine(topk_weights)
+        return self.y

@@ -1,0 +1,217 @@
+/*
+ * moe_ep.h -- C ABI of the MI355X (gfx950) MoE expert-parallel hot path,
+ * one GPU's share:
+ *
+ *   moe_dispatch_layout -> moe_permute -> moe_grouped_gemm_w13
+ *     -> (moe_silu_mul) -> moe_grouped_gemm_w2 -> moe_combine
+ *
+ * Pages cited (by title):
+ *   [EP]  "SGLang、NCCL 与 MoE EP：从职责边界到执行机制"
+ *   [ECB] "SGLang Expert Compute Backend：从接收布局到 Triton 专家计算"
+ *   [DEP] "DeepEP 架构与实现笔记"
+ *
+ * Conventions shared by every entry point
+ *   - Every pointer argument is DEVICE memory owned by the caller; the
+ *     library never allocates, frees or keeps a pointer after returning.
+ *   - Every call enqueues work on `stream` and returns without waiting for
+ *     the GPU.  Launch shapes depend only on the size arguments, never on
+ *     device-side counts, so the calls can be captured in a hipGraph and
+ *     replayed with new routing (the device re-derives all counts).
+ *   - Tensors are dense row-major, shapes as written below.  bf16 and
+ *     OCP e4m3fn ("float8_e4m3fn", largest finite 448) are stored as raw
+ *     16-/8-bit patterns.
+ *   - Argument errors are detected on the host and returned before anything
+ *     is enqueued (MOE_ERR_INVALID_ARG / MOE_ERR_UNSUPPORTED).  A launch
+ *     failure reported by the HIP runtime returns MOE_ERR_HIP.  Errors that
+ *     depend on data (capacity overflow, bad expert id) are written to
+ *     device memory by moe_dispatch_layout (see dev_status).
+ *   - Expert-major buffers: local expert e owns rows
+ *     [offsets[e], offsets[e] + counts[e]) -- a contiguous valid prefix of its
+ *     block ([EP] §2.3.4).  Rows outside these ranges ("padding") are never
+ *     read for a result and never written by any entry point.
+ *   - rows_cap is the number of rows of every expert-major buffer:
+ *     L*R with capacity R, or T*K with exact-fit offsets.
+ */
+#ifndef MOE_EP_H
+#define MOE_EP_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = -1,   /* null pointer, negative size, bad enum    */
+  MOE_ERR_UNSUPPORTED = -2,   /* valid but unsupported dtype/shape combo  */
+  MOE_ERR_WORKSPACE = -3,     /* workspace smaller than required          */
+  MOE_ERR_HIP = -5            /* the HIP runtime rejected a launch        */
+} moe_status;
+
+typedef enum moe_dtype {
+  MOE_F32 = 0,
+  MOE_BF16 = 1,
+  MOE_FP8_E4M3 = 2            /* OCP e4m3fn codes with fp32 group scales  */
+} moe_dtype;
+
+/* Epilogue of the gate/up GEMM. */
+typedef enum moe_w13_epilogue {
+  MOE_EPI_STORE_G = 0,        /* out = G [rows_cap, 2I] fp32               */
+  MOE_EPI_SILU_MUL = 1        /* out = Z = SiLU(G[:, :I]) * G[:, I:]       */
+} moe_w13_epilogue;
+
+/* Bits of dev_status[0] written by moe_dispatch_layout. */
+#define MOE_FLAG_CAPACITY 1      /* a local expert received more than R routes */
+#define MOE_FLAG_BAD_EXPERT_ID 2 /* an id was < -1 or >= E_global              */
+
+/* Human-readable name of a moe_status value (static string). */
+const char* moe_status_string(int status);
+
+/* ABI version; bumped on any signature change. */
+int moe_abi_version(void);
+
+/* Bytes of device workspace moe_dispatch_layout needs for (T, K, L). */
+size_t moe_dispatch_layout_workspace_bytes(int T, int K, int L);
+
+/*
+ * moe_dispatch_layout -- counts, offsets, slots and the reverse map.
+ *
+ * Defined by [EP] §2.3.4 (per-expert row allocator: a route to local
+ * expert e gets s = counter[e]++ and row q = offsets[e] + s, each expert's
+ * rows a contiguous prefix), [EP] §2.3.6 (reverse map (t,k) -> q, -1 for
+ * top-k entries not owned here) and [DEP] §9.4 (dispatch_convert: tokens,
+ * then top-k positions, in order).  Rows of one expert are ordered by the
+ * flattened route index i = t*K + k, so the result is unique and
+ * deterministic (the pages' atomic order is one of many valid orders).
+ *
+ *   topk_ids   [T,K] int32  global expert ids; -1 = no route
+ *   E_global   number of global experts; ids must lie in [-1, E_global)
+ *   expert_begin, L   this GPU owns global experts [expert_begin, expert_begin+L)
+ *   R          capacity rows per local expert (> 0), or 0 for exact-fit
+ *              offsets (offsets = exclusive prefix sum of counts, [ECB] §4.1)
+ *   BM         tile rows used for tile_offsets (> 0)
+ * Outputs (all fully rewritten on every call; stale contents never count):
+ *   counts       [L]    min(routes to e, R)            (exact-fit: routes to e)
+ *   offsets      [L+1]  e*R, or prefix sums of counts; offsets[L] = rows used
+ *   slot_of      [T,K]  row q of route (t,k), or -1 (no route, not local,
+ *                       bad id, or beyond capacity)
+ *   row_src      [rows_cap] t*K + k for valid rows, -1 for padding rows
+ *   tile_offsets [L+1]  prefix sums of ceil(counts[e] / BM)
+ *   dev_status   [2]    [0] = MOE_FLAG_* bits, [1] = routes dropped because
+ *                       of capacity.  Routes beyond capacity are never written.
+ *   workspace    >= moe_dispatch_layout_workspace_bytes(T, K, L) bytes
+ * Limits: 1 <= L <= 1024, T*K <= 2^30.
+ */
+moe_status moe_dispatch_layout(const int32_t* topk_ids, int T, int K, int E_global,
+                               int expert_begin, int L, int R, int BM,
+                               int32_t* counts, int32_t* offsets, int32_t* slot_of,
+                               int32_t* row_src, int32_t* tile_offsets, int32_t* dev_status,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * moe_permute -- fill the expert-major buffer from token rows.
+ *
+ * buf[slot_of[t,k], :] = x[t, :] for every (t,k) with slot_of >= 0
+ * ([EP] §2.3.4 recv_tokens[e, s, :] = payload; [DEP] §9.4 recv_x_all[m] =
+ * recv_x[token]).  With buf_dt == MOE_FP8_E4M3 each written row is quantised
+ * per group of 128 columns ([EP] §2.3.5 FP8 [L,M,H] + fp32 [L,M,H/128];
+ * recipe of [DEP] §11): amax = max|x| over the group clamped below at 1e-4,
+ * code = e4m3fn(x * (448/amax)) rounded to nearest even, scale = amax/448,
+ * every step a single fp32 operation.  Each token row is read once.
+ *
+ *   x          [T,H]  x_dt in {MOE_F32, MOE_BF16}
+ *   slot_of    [T,K]  from moe_dispatch_layout (values >= rows_cap are skipped)
+ *   buf        [rows_cap,H]  buf_dt: same as x_dt, or MOE_FP8_E4M3
+ *   buf_scales [rows_cap,H/128] fp32 when buf_dt == MOE_FP8_E4M3, else unused
+ * Limits: H % 128 == 0.  Padding rows of buf are left untouched.
+ */
+moe_status moe_permute(const void* x, moe_dtype x_dt, int T, int K, int H,
+                       const int32_t* slot_of, int64_t rows_cap,
+                       void* buf, moe_dtype buf_dt, float* buf_scales, hipStream_t stream);
+
+/*
+ * moe_grouped_gemm_w13 -- gate/up projection of every local expert.
+ *
+ * For each expert e and valid row q of e: G[q, n] = sum_k A[q,k] W13[e,n,k]
+ * ([ECB] §1.1: X_e [m_e,H] -> [m_e,2I]; §2.3: one grouped launch over all
+ * experts' valid rows; weights stored [expert, out, in], §3.5).  With FP8
+ * operands the block-wise scales apply per 128-wide K group ([ECB] §3.5):
+ * G[q,n] = sum_g a_scales[q,g] * w13_scales[e, n/128, g] * sum_{k in g} a8*w8,
+ * accumulated in fp32.  Only tiles that contain valid rows are computed (an
+ * in-kernel scheduler walks ceil(counts[e]/BM) row tiles per expert, [ECB]
+ * §2.5/§2.6); rows beyond counts[e] are never stored.
+ *
+ *   a          [rows_cap,H]  a_dt;  a_scales [rows_cap,H/128] fp32 for FP8
+ *   w13        [L,2I,H]      w_dt == a_dt; rows [0,I) are gate, [I,2I) up
+ *   w13_scales [L,2I/128,H/128] fp32 for FP8, else unused
+ *   counts, offsets  [L], [L+1] as produced by moe_dispatch_layout
+ *   epi == MOE_EPI_STORE_G:  out = G [rows_cap,2I], out_dt = MOE_F32
+ *   epi == MOE_EPI_SILU_MUL: out = Z [rows_cap,I] = SiLU(gate) * up computed
+ *        from the fp32 accumulators ([ECB] §3.6 non-interleaved gate/up;
+ *        §4.4 fusion of SiLU*up with the group quantisation); out_dt in
+ *        {MOE_F32, MOE_BF16, MOE_FP8_E4M3}; for FP8, out_scales
+ *        [rows_cap, I/128] fp32 get the same per-128 recipe as moe_permute.
+ * dtype pairs (a_dt = w_dt): F32, BF16, FP8_E4M3.  Limits: H % 128 == 0,
+ * I % 128 == 0, L <= 1024.
+ */
+moe_status moe_grouped_gemm_w13(const void* a, moe_dtype a_dt, const float* a_scales,
+                                const void* w13, moe_dtype w_dt, const float* w13_scales,
+                                const int32_t* counts, const int32_t* offsets, int L,
+                                int64_t rows_cap, int H, int I, moe_w13_epilogue epi,
+                                void* out, moe_dtype out_dt, float* out_scales,
+                                hipStream_t stream);
+
+/*
+ * moe_silu_mul -- Z = SiLU(G[:, :I]) * G[:, I:] on valid rows only
+ * ([ECB] §3.6: activation filtered to valid expert rows; Z re-quantised for
+ * the down GEMM with its own scales).  SiLU(v) = v / (1 + exp(-v)) in fp32.
+ *   g [rows_cap,2I] fp32;  z [rows_cap,I] z_dt in {F32, BF16, FP8_E4M3};
+ *   z_scales [rows_cap,I/128] fp32 for FP8 (recipe of moe_permute).
+ * Limits: I % 128 == 0.
+ */
+moe_status moe_silu_mul(const float* g, const int32_t* counts, const int32_t* offsets, int L,
+                        int64_t rows_cap, int I, void* z, moe_dtype z_dt, float* z_scales,
+                        hipStream_t stream);
+
+/*
+ * moe_grouped_gemm_w2 -- down projection of every local expert.
+ *
+ * out[q, n] = sum_k Z[q,k] W2[e,n,k] for valid rows q of expert e
+ * ([ECB] §1.1: [m_e,I] -> [m_e,H]; §3.6: same grouping as the gate/up GEMM,
+ * K = I), block-FP8 scaled as in moe_grouped_gemm_w13, fp32 accumulation,
+ * stored as out_dt; results stay at row q ([ECB] §3.7).  The router weight
+ * is NOT applied here ([EP] §1.1).
+ *   z [rows_cap,I] z_dt;  z_scales [rows_cap,I/128] fp32 for FP8
+ *   w2 [L,H,I] w_dt == z_dt;  w2_scales [L,H/128,I/128] fp32 for FP8
+ *   out [rows_cap,H] out_dt in {MOE_F32, MOE_BF16}
+ * Limits: H % 128 == 0, I % 128 == 0, L <= 1024.
+ */
+moe_status moe_grouped_gemm_w2(const void* z, moe_dtype z_dt, const float* z_scales,
+                               const void* w2, moe_dtype w_dt, const float* w2_scales,
+                               const int32_t* counts, const int32_t* offsets, int L,
+                               int64_t rows_cap, int H, int I,
+                               void* out, moe_dtype out_dt, hipStream_t stream);
+
+/*
+ * moe_combine -- weighted gather-sum back to token order.
+ *
+ * y[t, :] = sum over k with slot_of[t,k] >= 0 of topk_weights[t,k] *
+ * expert_out[slot_of[t,k], :], accumulated in fp32 in k order, stored as
+ * y_dt; 0 for a token with no local route ([EP] §1.1: weights multiply
+ * expert outputs; §2.3.6: follow the (t,k) -> q map back; [DEP] §9.4
+ * combine_convert).
+ *   expert_out [rows_cap,H] eo_dt in {F32, BF16};  slot_of [T,K];
+ *   topk_weights [T,K] fp32;  y [T,H] y_dt in {F32, BF16}
+ * Limits: H % 8 == 0.
+ */
+moe_status moe_combine(const void* expert_out, moe_dtype eo_dt, const int32_t* slot_of,
+                       const float* topk_weights, int T, int K, int H, int64_t rows_cap,
+                       void* y, moe_dtype y_dt, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_EP_H */

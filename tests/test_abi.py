@@ -1,0 +1,176 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/moe_ep.h declares, and rejects bad arguments on the host before
+enqueueing anything (all calls below return before any HIP runtime call)."""
+import ctypes
+import os
+import re
+import subprocess
+import sys
+from pathlib import Path
+
+import pytest
+
+ROOT = Path(__file__).resolve().parents[1]
+HEADER = ROOT / "include" / "moe_ep.h"
+LIB = ROOT / "combine_top_expert_amd" / "libmoe_ep.so"
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, -1, -2, -3
+
+
+def declared_functions():
+    text = HEADER.read_text()
+    return sorted(set(re.findall(r"^\s*(?:moe_status|size_t|const char\*|int)\s+(moe_\w+)\s*\(",
+                                 text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not LIB.exists():
+        from combine_top_expert_amd.build import build
+        build(verbose=False)
+    return ctypes.CDLL(str(LIB))
+
+
+def test_header_declares_the_six_entry_points():
+    fns = declared_functions()
+    for name in ["moe_dispatch_layout", "moe_permute", "moe_grouped_gemm_w13", "moe_silu_mul",
+                 "moe_grouped_gemm_w2", "moe_combine"]:
+        assert name in fns
+    assert len(fns) == 9
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", str(LIB)], capture_output=True, text=True)
+    exported = set(re.findall(r" T (moe_\w+)$", out.stdout, flags=re.M))
+    assert set(declared_functions()) <= exported
+    # C linkage: no mangled moe symbols leak into the ABI
+    assert not re.search(r" T _Z\w*moe_(dispatch_layout|permute|combine)", out.stdout)
+
+
+def test_status_strings_and_version(lib):
+    lib.moe_status_string.restype = ctypes.c_char_p
+    assert lib.moe_status_string(0) == b"MOE_OK"
+    assert lib.moe_status_string(-2) == b"MOE_ERR_UNSUPPORTED"
+    assert lib.moe_status_string(12345) == b"MOE_ERR_UNKNOWN"
+    assert lib.moe_abi_version() == 1
+
+
+def test_workspace_bytes(lib):
+    f = lib.moe_dispatch_layout_workspace_bytes
+    f.restype = ctypes.c_size_t
+    # ceil(T*K / 1024) blocks, L counters each, a flag per block, 64 spare ints
+    for T, K, L in [(8192, 8, 32), (16384, 6, 64), (0, 4, 8), (1, 1, 1)]:
+        nblk = -(-(T * K) // 1024)
+        assert f(T, K, L) == 4 * (nblk * L + nblk + 64)
+    assert f(-1, 2, 3) == 0
+
+
+def P(v=1):
+    return ctypes.c_void_p(v)
+
+
+def layout_call(lib, T=4, K=2, E=8, e0=0, L=8, R=16, BM=128, ws_bytes=1 << 20, null=None):
+    f = lib.moe_dispatch_layout
+    f.restype = ctypes.c_int
+    ptrs = [P() for _ in range(8)]
+    if null is not None:
+        ptrs[null] = None
+    ids, counts, offsets, slot_of, row_src, tiles, status, ws = ptrs
+    return f(ids, T, K, E, e0, L, R, BM, counts, offsets, slot_of, row_src, tiles, status, ws,
+             ctypes.c_size_t(ws_bytes), None)
+
+
+def test_layout_argument_errors(lib):
+    assert layout_call(lib, L=0) == INVALID
+    assert layout_call(lib, L=2000, E=4000) == INVALID       # L beyond 1024
+    assert layout_call(lib, e0=4, L=8, E=8) == INVALID       # experts beyond E
+    assert layout_call(lib, R=-1) == INVALID
+    assert layout_call(lib, BM=0) == INVALID
+    assert layout_call(lib, ws_bytes=4) == WORKSPACE
+    for i in range(8):
+        assert layout_call(lib, null=i) == INVALID, i
+
+
+def test_permute_argument_errors(lib):
+    f = lib.moe_permute
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                  ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
+                  ctypes.c_void_p]
+    assert f(P(), 1, 4, 2, 100, P(), 8, P(), 1, None, None) == UNSUPPORTED   # H % 128
+    assert f(P(), 1, 4, 2, 256, P(), 8, P(), 0, None, None) == UNSUPPORTED   # bf16 -> fp32
+    assert f(P(), 2, 4, 2, 256, P(), 8, P(), 2, P(), None) == UNSUPPORTED   # fp8 input
+    assert f(P(), 1, 4, 2, 256, P(), 8, P(), 2, None, None) == INVALID      # fp8 without scales
+    assert f(P(), 7, 4, 2, 256, P(), 8, P(), 1, None, None) == INVALID      # bad dtype enum
+    assert f(None, 1, 0, 2, 256, None, 8, None, 1, None, None) == OK        # T = 0: nothing to do
+
+
+def test_gemm_argument_errors(lib):
+    w13 = lib.moe_grouped_gemm_w13
+    w13.restype = ctypes.c_int
+    w13.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+                    ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int64,
+                    ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_int,
+                    ctypes.c_void_p, ctypes.c_void_p]
+
+    def call(a_dt=2, w_dt=2, H=256, I=128, epi=1, out_dt=2, L=2, scales=True):
+        s = P() if scales else None
+        return w13(P(), a_dt, s, P(), w_dt, s, P(), P(), L, 256, H, I, epi, P(), out_dt, s, None)
+
+    assert call(a_dt=1, w_dt=2) == UNSUPPORTED
+    assert call(H=200) == UNSUPPORTED
+    assert call(I=100) == UNSUPPORTED
+    assert call(epi=0, out_dt=1) == UNSUPPORTED      # G is always fp32
+    assert call(epi=5) == INVALID
+    assert call(L=0) == INVALID
+    assert call(scales=False) == INVALID
+    w2 = lib.moe_grouped_gemm_w2
+    w2.restype = ctypes.c_int
+    w2.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+                   ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int64,
+                   ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    assert w2(P(), 1, None, P(), 1, None, P(), P(), 2, 256, 256, 128, P(), 2, None) == UNSUPPORTED
+    assert w2(P(), 0, None, P(), 1, None, P(), P(), 2, 256, 256, 128, P(), 1, None) == UNSUPPORTED
+
+
+def test_combine_and_silu_argument_errors(lib):
+    c = lib.moe_combine
+    c.restype = ctypes.c_int
+    c.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+                  ctypes.c_int, ctypes.c_int, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int,
+                  ctypes.c_void_p]
+    assert c(P(), 1, P(), P(), 4, 2, 100, 8, P(), 1, None) == UNSUPPORTED    # H % 8
+    assert c(P(), 2, P(), P(), 4, 2, 256, 8, P(), 1, None) == UNSUPPORTED    # fp8 outputs
+    assert c(P(), 1, None, P(), 4, 2, 256, 8, P(), 1, None) == INVALID
+    s = lib.moe_silu_mul
+    s.restype = ctypes.c_int
+    s.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int64,
+                  ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    assert s(P(), P(), P(), 2, 256, 100, P(), 1, None, None) == UNSUPPORTED
+    assert s(P(), P(), P(), 2, 256, 128, P(), 2, None, None) == INVALID
+
+
+def test_python_binding_loads_and_matches_header(lib):
+    import combine_top_expert_amd as ep
+    for name in declared_functions():
+        assert callable(getattr(ep, name)), name
+    assert ep.moe_abi_version() == 1
+    assert ep.moe_status_string(-1) == "MOE_ERR_INVALID_ARG"
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    env = dict(os.environ, MOE_EP_LIB=str(tmp_path / "missing.so"))
+    r = subprocess.run([sys.executable, "-c", "import combine_top_expert_amd"], cwd=ROOT, env=env,
+                       capture_output=True, text=True)
+    assert r.returncode != 0 and "not built" in r.stderr
+
+
+def test_product_never_touches_the_oracle():
+    pkg = ROOT / "combine_top_expert_amd"
+    for f in list(pkg.rglob("*.py")) + list(pkg.rglob("*.hip")) + list(pkg.rglob("*.cpp")) + \
+            list(pkg.rglob("*.h")):
+        text = f.read_text()
+        assert not re.search(r"^\s*(from|import)\s+(oracle|workloads)\b", text, flags=re.M), f
+        assert "oracle/" not in text, f

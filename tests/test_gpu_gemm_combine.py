@@ -1,0 +1,233 @@
+"""GPU parity: grouped GEMMs, SiLU*up and combine, stage by stage.
+
+Each stage gets the oracle's own inputs for that stage (so upstream rounding
+differences do not mix in) and is compared element by element on every valid
+row.  Tolerances: the GPU accumulates in fp32 in a different order than the
+oracle's float64 dots, so G and expert outputs differ by a few fp32 ulps
+(bound 1e-5 relative L2 on bf16/fp32 matrix cores, 1e-4 on FP8 ones, whose
+per-instruction accumulation is below fp32 precision; plus the bf16 half-ulp
+where outputs are rounded to bf16); FP8 re-quantisation of Z may move a code by one step where z lies on a
+rounding boundary, so Z is compared by value.  Combine, given identical
+expert outputs, is bit-exact (same fp32 operations in the same order)."""
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import (GEMM_REL_L2, announce, dev, host_bits, host_vals, layer_shape, need_gpu,
+                      rel_l2, upload_weights)
+from oracle import formats as F
+from oracle import moe
+from workloads import get_config, make_routing, make_share_buffer, make_workload
+
+pytestmark = pytest.mark.gpu
+
+GEMM_CASES = ["toy_fp32", "share_bf16", "toy_bf16_fp8w", "decode_fp8_small", "prefill_fp8_small",
+              "skewed_bf16_small"]
+
+
+@pytest.fixture(scope="module")
+def ep():
+    need_gpu()
+    import combine_top_expert_amd as ep
+    return ep
+
+
+def oracle_stage_inputs(wl):
+    """The oracle's expert-major buffer (valid rows), counts and offsets."""
+    cfg = wl.cfg
+    if cfg.routing == "given":
+        sh = wl.share
+        rows = moe.valid_rows(sh["counts"], sh["offsets"])
+        return {"counts": sh["counts"], "offsets": sh["offsets"], "rows": rows,
+                "data": sh["buf"][rows], "scales": None, "slot_of": sh["slot_of"]}
+    lay = moe.dispatch_layout(wl.ids, cfg.E, cfg.expert_begin, cfg.L, cfg.R)
+    perm = moe.permute(wl.x, cfg.act, lay["row_src"], cfg.K, cfg.buf_dt)
+    return {"counts": lay["counts"], "offsets": lay["offsets"], "rows": perm["rows"],
+            "data": perm["data"], "scales": perm.get("scales"), "slot_of": lay["slot_of"]}
+
+
+def make_layer_with_buffer(wl, inp, fused):
+    from combine_top_expert_amd.pipeline import MoELayer
+    cfg = wl.cfg
+    layer = MoELayer(layer_shape(cfg), fused=fused)
+    upload_weights(layer, wl)
+    layer.counts.copy_(dev(inp["counts"]))
+    layer.offsets.copy_(dev(inp["offsets"]))
+    layer.slot_of.copy_(dev(inp["slot_of"]))
+    # NaN in every padding row of the A buffer: it must never reach a result
+    full = np.zeros((cfg.rows_cap, cfg.H), inp["data"].dtype)
+    if cfg.buf_dt == "fp8":
+        full[:] = 0x7F
+    elif cfg.buf_dt == "bf16":
+        full[:] = 0xFFFF
+    else:
+        full[:] = np.nan
+    full[inp["rows"]] = inp["data"]
+    layer.buf.copy_(dev(full, "bf16" if cfg.buf_dt == "bf16" else None))
+    if cfg.buf_dt == "fp8":
+        sc = np.full((cfg.rows_cap, cfg.H // 128), np.nan, np.float32)
+        sc[inp["rows"]] = inp["scales"]
+        layer.buf_scales.copy_(dev(sc))
+    return layer
+
+
+def oracle_mlp(wl, inp):
+    cfg = wl.cfg
+    a_vals = moe.buffer_values(inp["data"], cfg.buf_dt, inp["scales"])
+    e_of = {int(q): int(np.searchsorted(inp["offsets"], q, side="right") - 1) for q in inp["rows"]}
+    a_by = {int(q): a_vals[i] for i, q in enumerate(inp["rows"])}
+    return moe.expert_mlp_rows(cfg, a_by, e_of, moe.ExpertWeights(cfg, wl.w))
+
+
+@pytest.mark.parametrize("name", GEMM_CASES)
+def test_gemm_w13_store_g(ep, name):
+    announce("w13 G", name)
+    wl = make_workload(name)
+    inp = oracle_stage_inputs(wl)
+    layer = make_layer_with_buffer(wl, inp, fused=False)
+    layer.g.fill_(float("nan"))
+    layer.gemm_w13()
+    torch.cuda.synchronize()
+    ref = oracle_mlp(wl, inp)
+    g = layer.g.cpu().numpy()
+    rows = inp["rows"]
+    ref_g = np.stack([ref["G"][int(q)] for q in rows])
+    err = rel_l2(g[rows], ref_g)
+    print(f"[metric] G {name} rel_l2={err:.3e}", flush=True)
+    assert err < GEMM_REL_L2[wl.cfg.wdt]
+    pad = np.ones(wl.cfg.rows_cap, bool)
+    pad[rows] = False
+    assert np.all(np.isnan(g[pad])), "padding rows of G were written"
+
+
+@pytest.mark.parametrize("name", GEMM_CASES)
+def test_silu_mul_standalone(ep, name):
+    """moe_silu_mul on the oracle's G: fp32/bf16 Z to one rounding step,
+    FP8 Z codes per the recipe (value comparison)."""
+    announce("silu_mul", name)
+    wl = make_workload(name)
+    cfg = wl.cfg
+    inp = oracle_stage_inputs(wl)
+    ref = oracle_mlp(wl, inp)
+    layer = make_layer_with_buffer(wl, inp, fused=False)
+    rows = inp["rows"]
+    g = np.full((cfg.rows_cap, 2 * cfg.I), np.nan, np.float32)
+    g[rows] = np.stack([ref["G"][int(q)] for q in rows])
+    layer.g.copy_(dev(g))
+    layer.silu_mul()
+    torch.cuda.synchronize()
+    z_ref = moe.silu_mul(g[rows], cfg.I)
+    if cfg.z_dt == "fp8":
+        codes = host_bits(layer.z)[rows]
+        sc = layer.z_scales.cpu().numpy()[rows]
+        zv = F.dequant_fp8_groups(codes, sc)
+        rc, rs = F.quant_fp8_groups(z_ref)
+        assert rel_l2(zv, F.dequant_fp8_groups(rc, rs)) < 1e-3
+        assert np.mean(codes == rc) > 0.999
+    elif cfg.z_dt == "bf16":
+        zb = host_bits(layer.z)[rows].astype(np.int32)
+        assert np.max(np.abs(zb - F.f32_to_bf16(z_ref).astype(np.int32))) <= 1
+    else:
+        assert rel_l2(host_vals(layer.z)[rows], z_ref) < 1e-6
+
+
+@pytest.mark.parametrize("name", GEMM_CASES)
+def test_gemm_w13_fused_silu(ep, name):
+    announce("w13 fused", name)
+    wl = make_workload(name)
+    cfg = wl.cfg
+    inp = oracle_stage_inputs(wl)
+    ref = oracle_mlp(wl, inp)
+    layer = make_layer_with_buffer(wl, inp, fused=True)
+    layer.gemm_w13()
+    torch.cuda.synchronize()
+    rows = inp["rows"]
+    if cfg.z_dt == "fp8":
+        zv = F.dequant_fp8_groups(host_bits(layer.z)[rows], layer.z_scales.cpu().numpy()[rows])
+        zr = F.dequant_fp8_groups(np.stack([ref["Z"][int(q)] for q in rows]),
+                                  np.stack([ref["Zs"][int(q)] for q in rows]))
+        assert rel_l2(zv, zr) < 5e-3
+    elif cfg.z_dt == "bf16":
+        zv = host_vals(layer.z)[rows]
+        zr = F.bf16_to_f32(np.stack([ref["Z"][int(q)] for q in rows]))
+        assert rel_l2(zv, zr) < 5e-3
+    else:
+        zv = host_vals(layer.z)[rows]
+        zr = np.stack([ref["Z"][int(q)] for q in rows])
+        assert rel_l2(zv, zr) < 1e-5
+
+
+@pytest.mark.parametrize("name", GEMM_CASES)
+def test_gemm_w2(ep, name):
+    """Down GEMM on the oracle's Z."""
+    announce("w2", name)
+    wl = make_workload(name)
+    cfg = wl.cfg
+    inp = oracle_stage_inputs(wl)
+    ref = oracle_mlp(wl, inp)
+    layer = make_layer_with_buffer(wl, inp, fused=True)
+    rows = inp["rows"]
+    zfull = np.zeros((cfg.rows_cap, cfg.I), {"fp8": np.uint8, "bf16": np.uint16, "f32": np.float32}[cfg.z_dt])
+    zfull[rows] = np.stack([ref["Z"][int(q)] for q in rows])
+    layer.z.copy_(dev(zfull, "bf16" if cfg.z_dt == "bf16" else None))
+    if cfg.z_dt == "fp8":
+        zs = np.zeros((cfg.rows_cap, cfg.I // 128), np.float32)
+        zs[rows] = np.stack([ref["Zs"][int(q)] for q in rows])
+        layer.z_scales.copy_(dev(zs))
+    if layer.out.dtype == torch.bfloat16:
+        layer.out.view(torch.int16).fill_(-1)
+    else:
+        layer.out.fill_(float("nan"))
+    layer.gemm_w2()
+    torch.cuda.synchronize()
+    out = host_vals(layer.out)
+    ref_out = np.stack([ref["out"][int(q)] for q in rows])
+    # bf16 outputs: a different fp32 accumulation order can move the rounding
+    # by one bf16 step (relative 2^-8) on a few elements
+    tol = 1e-5 if cfg.out_dt == "f32" else 2e-3
+    assert rel_l2(out[rows], ref_out) < tol
+    pad = np.ones(cfg.rows_cap, bool)
+    pad[rows] = False
+    assert np.all(np.isnan(out[pad])), "padding rows of the expert output were written"
+
+
+@pytest.mark.parametrize("name", GEMM_CASES + ["decode_fp8", "skewed_bf16"])
+def test_combine_bit_exact(ep, name):
+    """Combine of the oracle's expert outputs equals the oracle bit for bit."""
+    announce("combine", name)
+    cfg = get_config(name)
+    rng = np.random.default_rng(0)
+    if cfg.routing == "given":
+        sh = make_share_buffer(cfg)
+        slot_of, weights = sh["slot_of"], sh["weights"]
+    else:
+        ids, weights = make_routing(cfg)
+        slot_of = moe.dispatch_layout(ids, cfg.E, cfg.expert_begin, cfg.L, cfg.R)["slot_of"]
+    vals = rng.standard_normal((cfg.rows_cap, cfg.H)).astype(np.float32)
+    if cfg.out_dt == "bf16":
+        bits = F.f32_to_bf16(vals)
+        vals = F.bf16_to_f32(bits)
+        eo = dev(bits, "bf16")
+    else:
+        eo = dev(vals)
+    out_rows = {q: vals[q] for q in range(cfg.rows_cap)}
+    ref = moe.combine(out_rows, slot_of, weights, cfg.out_dt)
+    y = torch.full((cfg.T, cfg.H), float("nan"), dtype=eo.dtype, device="cuda")
+    ep.moe_combine(eo, dev(slot_of), dev(weights), y)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_vals(y), ref)
+
+
+def test_combine_weighted_sum_fact(ep, gold):
+    """0.25 * 4 + 0.75 * 12 = 10 through the device combine."""
+    announce("combine 4/12")
+    g = gold("combine_weighted_sum.json")
+    eo = torch.zeros(4, 8, device="cuda")
+    eo[1, 0], eo[3, 0] = g["expert_outputs"][0], g["expert_outputs"][1]
+    slot_of = torch.tensor([[1, 3], [-1, -1]], dtype=torch.int32, device="cuda")
+    w = torch.tensor([g["weights"], [0.5, 0.5]], dtype=torch.float32, device="cuda")
+    y = torch.full((2, 8), 7.0, device="cuda")
+    ep.moe_combine(eo, slot_of, w, y)
+    torch.cuda.synchronize()
+    assert y[0, 0].item() == g["combined"]
+    assert torch.all(y[1] == 0)         # no local route -> 0
