@@ -21,18 +21,26 @@
 // halves are the gate block n0 + [0,128) and the matching up block
 // I + n0 + [0,128), so one lane holds gate and up of the same (row, column)
 // and SiLU(gate)*up needs no data exchange.  For W2 the halves are two
-// adjacent 128-column blocks.  Four waves in a 2x2 grid each own 64 rows x
-// (64 columns of each half) = 32 MFMA 16x16 tiles.
+// adjacent 128-column blocks.  Eight waves (two per SIMD, so one wave's LDS
+// reads overlap the other's matrix work) in a 2x4 grid each own 64 rows x
+// (32 columns of each half) = 16 MFMA 16x16 tiles.
 //
 // K loop.  One stage = 128 bytes of K per row: 128 FP8, 64 bf16 or 32 fp32
 // values -- for FP8 exactly one activation / weight scale group.  Each
 // lane's MFMA operand is 32 contiguous bytes of one row of the stage, so
 // the same LDS fragment feeds one 16x16x128 FP8 MFMA, two 16x16x32 bf16
 // MFMAs or eight 16x16x4 fp32 MFMAs (A and B use the same K mapping, so the
-// dot products pair up).  Stages are double-buffered in LDS with a 16-byte
-// XOR swizzle (chunk c of row r at chunk c ^ (r & 7)) so fragment reads and
-// stage writes are bank-conflict free; the next stage is fetched into
-// registers while the current one is multiplied.
+// dot products pair up).
+//
+// Stages move HBM -> LDS by direct-to-LDS loads (global_load_lds_dwordx4:
+// lane l's 16 bytes land at base + 16*l), three stages deep, so two stages
+// are in flight while the third is multiplied and no VGPR holds staged data.
+// A stage row is 128 bytes in a 16-byte XOR swizzle (chunk c of row r at
+// chunk c ^ ((r >> 1) & 7), bank-conflict free on the 64-bank LDS); the
+// swizzle is applied by choosing which source chunk each lane fetches.  Fragment reads are issued as ds_read_b128 in inline
+// assembly that ends with its own lgkmcnt wait, so the compiler never
+// inserts a full vmcnt wait (which would drain the loads still in flight);
+// stage completion is tracked by hand with vmcnt and a workgroup barrier.
 //
 // FP8 scaling.  Per stage g every 16x16 FP8 product P_g is formed from a
 // zero accumulator and folded in as acc += P_g * (a_scale[row, g] *
@@ -49,11 +57,17 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));   // 16 bytes in 4 VGPRs
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;
 constexpr int BM = 128;            // rows per tile
 constexpr int BH = 128;            // columns per half
 constexpr int KB = 128;            // bytes of K per stage and row
 constexpr int kMaxL = 1024;
+constexpr int NST = 3;             // LDS ring depth
+constexpr int A_BYTES = BM * KB;                   // 16 KB
+constexpr int B_BYTES = 2 * BH * KB;               // 32 KB
+constexpr int AS_BYTES = BM * 4;                   // FP8 activation scales
+constexpr int STAGE = A_BYTES + B_BYTES + AS_BYTES;
+constexpr int kRsrcWord3 = 0x00020000;             // raw buffer: 32-bit data format
 
 enum Dt { DT_F32 = 0, DT_BF16 = 1, DT_FP8 = 2 };
 enum Epi { EPI_STORE_F32 = 0, EPI_STORE_BF16 = 1, EPI_SILU_F32 = 2, EPI_SILU_BF16 = 3, EPI_SILU_FP8 = 4 };
@@ -77,25 +91,51 @@ struct GemmArgs {
   int ldo;               // output row length in elements
 };
 
-struct Stage {
-  uint8_t a[BM * KB];          // 16 KB
-  uint8_t b[2 * BH * KB];      // 32 KB
-  float as[BM];                // A scales of this stage (FP8)
-};
-
-struct Smem {
-  Stage st[2];
-  int mt_prefix[kMaxL + 1];    // row-tile prefix over experts
-  float amax[2][BM];           // FP8 SiLU epilogue: per-row amax of each wave column
-};
-
-__device__ __forceinline__ int swz(int row, int chunk) { return row * KB + ((chunk ^ (row & 7)) << 4); }
-
-// 32 bytes of row `row`, K quarter `kq` (bytes 32*kq .. 32*kq+31) of a stage
-__device__ __forceinline__ void frag(const uint8_t* base, int row, int kq, u4& lo, u4& hi) {
-  lo = *reinterpret_cast<const u4*>(base + swz(row, 2 * kq));
-  hi = *reinterpret_cast<const u4*>(base + swz(row, 2 * kq + 1));
+// Rows of expert e that exist: counts[e] clipped to the buffer, so a tile
+// never reaches past rows_cap even for inconsistent counts/offsets.
+__device__ __forceinline__ int eff_count(const GemmArgs& p, int e) {
+  const int64_t off = p.offsets[e];
+  if (off < 0 || off >= p.rows_cap) return 0;
+  return static_cast<int>(max<int64_t>(0, min<int64_t>(p.counts[e], p.rows_cap - off)));
 }
+
+// s_waitcnt immediate for "vmcnt <= n" with the other counters left alone
+template <int N> struct VmCnt {
+  static constexpr int imm = (N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8);
+};
+
+// byte address of a __shared__ object inside the workgroup's LDS
+__device__ __forceinline__ uint32_t lds_u32(const void* p) {
+  typedef const __attribute__((address_space(3))) uint8_t* lds_ptr;
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr)(p)));
+}
+
+// Eight 16-byte LDS reads (two per MFMA operand fragment of 4 sub-tiles)
+// from two per-lane base addresses, then wait for them.
+#define MOE_DS8(o, a0, a1, I0, I1, I2, I3)                                                \
+  asm volatile(                                                                            \
+      "ds_read_b128 %0, %8 offset:" #I0 "\n"                                              \
+      "ds_read_b128 %1, %9 offset:" #I0 "\n"                                              \
+      "ds_read_b128 %2, %8 offset:" #I1 "\n"                                              \
+      "ds_read_b128 %3, %9 offset:" #I1 "\n"                                              \
+      "ds_read_b128 %4, %8 offset:" #I2 "\n"                                              \
+      "ds_read_b128 %5, %9 offset:" #I2 "\n"                                              \
+      "ds_read_b128 %6, %8 offset:" #I3 "\n"                                              \
+      "ds_read_b128 %7, %9 offset:" #I3 "\n"                                              \
+      "s_waitcnt lgkmcnt(0)"                                                               \
+      : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]),     \
+        "=&v"(o[6]), "=&v"(o[7])                                                           \
+      : "v"(a0), "v"(a1))
+
+#define MOE_DS4(o, a, I0, I1, I2, I3)                                                      \
+  asm volatile(                                                                            \
+      "ds_read_b128 %0, %4 offset:" #I0 "\n"                                              \
+      "ds_read_b128 %1, %4 offset:" #I1 "\n"                                              \
+      "ds_read_b128 %2, %4 offset:" #I2 "\n"                                              \
+      "ds_read_b128 %3, %4 offset:" #I3 "\n"                                              \
+      "s_waitcnt lgkmcnt(0)"                                                               \
+      : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3])                                 \
+      : "v"(a))
 
 template <int DT>
 __device__ __forceinline__ v4f mma_stage(const u4& alo, const u4& ahi, const u4& blo,
@@ -123,66 +163,63 @@ __device__ __forceinline__ v4f mma_stage(const u4& alo, const u4& ahi, const u4&
   }
 }
 
-// Rows of expert e that exist: counts[e] clipped to the buffer, so a tile
-// never reaches past rows_cap even for inconsistent counts/offsets.
-__device__ __forceinline__ int eff_count(const GemmArgs& p, int e) {
-  const int64_t off = p.offsets[e];
-  if (off < 0 || off >= p.rows_cap) return 0;
-  return static_cast<int>(max<int64_t>(0, min<int64_t>(p.counts[e], p.rows_cap - off)));
-}
+__shared__ __attribute__((aligned(16))) uint8_t s_ring[NST * STAGE];
+__shared__ int s_mt_prefix[kMaxL + 1];
+__shared__ float s_amax[4][BM];
+__shared__ int s_part[kThreads];
 
-// Tile id -> (expert, column block, row tile).  mt_prefix[e] = sum of row
+// Tile id -> (expert, column block, row tile).  s_mt_prefix[e] = sum of row
 // tiles of experts < e; tile ids are expert-major, then column block, then
 // row tile.
-__device__ __forceinline__ void decode_tile(const Smem& sm, int L, int nb_count, int t, int& e,
-                                            int& nb, int& mt) {
-  int lo = 0, hi = L;           // largest e with mt_prefix[e]*nb_count <= t
+__device__ __forceinline__ void decode_tile(int L, int nb_count, int t, int& e, int& nb, int& mt) {
+  int lo = 0, hi = L;           // largest e with s_mt_prefix[e]*nb_count <= t
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
-    if (sm.mt_prefix[mid] * nb_count <= t) lo = mid; else hi = mid;
+    if (s_mt_prefix[mid] * nb_count <= t) lo = mid; else hi = mid;
   }
   e = lo;
-  const int mte = sm.mt_prefix[e + 1] - sm.mt_prefix[e];
-  const int local = t - sm.mt_prefix[e] * nb_count;
+  const int mte = s_mt_prefix[e + 1] - s_mt_prefix[e];
+  const int local = t - s_mt_prefix[e] * nb_count;
   nb = local / mte;
   mt = local - nb * mte;
 }
 
 template <int DT, int EPI>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs p) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem_raw[];
-  Smem& sm = *reinterpret_cast<Smem*>(smem_raw);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave & 1;       // 64-row slice
-  const int wn = wave >> 1;      // 64-column slice of each half
+  // wave-uniform by construction; readfirstlane tells the compiler so, which
+  // keeps the staged-load offsets in scalar registers (no per-load loop)
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave & 1;       // 64-row slice of the tile
+  const int wn = wave >> 1;      // 32-column slice of each half
   constexpr int ESZ = DT == DT_FP8 ? 1 : (DT == DT_BF16 ? 2 : 4);
+  constexpr bool kFp8 = DT == DT_FP8;
+  constexpr int NLOAD = kFp8 ? 7 : 6;      // direct-to-LDS loads per wave per stage
 
   // ---- tile map: row tiles per expert, prefix over experts (block scan)
   {
-    __shared__ int part[kThreads];
     const int per = (p.L + kThreads - 1) / kThreads;
     const int e0 = tid * per;
     int s = 0;
     for (int e = e0; e < min(e0 + per, p.L); ++e) s += (eff_count(p, e) + BM - 1) / BM;
-    part[tid] = s;
+    s_part[tid] = s;
     __syncthreads();
     for (int d = 1; d < kThreads; d <<= 1) {
-      const int v = tid >= d ? part[tid - d] : 0;
+      const int v = tid >= d ? s_part[tid - d] : 0;
       __syncthreads();
-      part[tid] += v;
+      s_part[tid] += v;
       __syncthreads();
     }
-    int run = part[tid] - s;     // exclusive prefix of this thread's range
+    int run = s_part[tid] - s;     // exclusive prefix of this thread's range
     for (int e = e0; e < min(e0 + per, p.L); ++e) {
-      sm.mt_prefix[e] = run;
+      s_mt_prefix[e] = run;
       run += (eff_count(p, e) + BM - 1) / BM;
     }
-    if (tid == kThreads - 1) sm.mt_prefix[p.L] = part[kThreads - 1];
+    if (tid == kThreads - 1) s_mt_prefix[p.L] = s_part[kThreads - 1];
     __syncthreads();
   }
-  const int n_tiles = sm.mt_prefix[p.L] * p.nb_count;
+  const int n_tiles = s_mt_prefix[p.L] * p.nb_count;
   int t_begin, t_end, t_step;
   if (gridDim.x >= 8 && (gridDim.x & 7) == 0) {
     const int xcd = blockIdx.x & 7;
@@ -200,129 +237,163 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs p) {
   const int kgroups = p.K / 128;              // FP8 scale groups along K
   const int64_t lda = static_cast<int64_t>(p.K) * ESZ;
 
+  // Stage layout: chunk c (16 bytes) of row r sits at chunk c ^ swz(r) with
+  // swz(r) = (r >> 1) & 7.  A 16-row fragment read (16 lanes, one 16-byte
+  // chunk each, rows r0..r0+15 with r0 % 16 == 0) then touches 16 distinct
+  // 4-bank groups of the 64-bank LDS, and a direct-to-LDS load writes 1 KB
+  // contiguously.  Lane l of a staging load fills row srow = l >> 3 of an
+  // 8-row group g, physical chunk l & 7; swz of that row is
+  // 4*(g & 1) + (srow >> 1), so the fetched chunk depends on g's parity.
+  const int srow = lane >> 3;
+  const int voff_e = static_cast<int>(srow * lda) + (((lane & 7) ^ (srow >> 1)) << 4);
+  const int voff_o = static_cast<int>(srow * lda) + (((lane & 7) ^ ((4 + (srow >> 1)) & 7)) << 4);
+  const int soff = (lane & 15) * kgroups * 4;    // A-scale row of this lane (FP8)
+  // fragment reads: row (lane & 15) of a 16-row block, bytes 32*(lane>>4)..+32
+  const int frow = lane & 15;
+  const int fc0 = ((2 * (lane >> 4)) ^ (frow >> 1)) << 4;
+  const int fc1 = ((2 * (lane >> 4) + 1) ^ (frow >> 1)) << 4;
+  const uint32_t ring = lds_u32(s_ring);
+
   for (int t = t_begin; t < t_end; t += t_step) {
     int e, nb, mt;
-    decode_tile(sm, p.L, p.nb_count, t, e, nb, mt);
+    decode_tile(p.L, p.nb_count, t, e, nb, mt);
     const int rows_valid = min(BM, eff_count(p, e) - mt * BM);
     const int64_t row0 = static_cast<int64_t>(p.offsets[e]) + static_cast<int64_t>(mt) * BM;
     const int n0 = nb * p.nb_stride;
     const bool half1 = n0 + p.half_stride < p.N;
-    const uint8_t* Wexp = p.W + static_cast<int64_t>(e) * p.N * lda;
 
-    // global source pointers of this thread's stage chunks
-    const int cch = tid & 7;
-    const uint8_t* asrc[4];
-    const uint8_t* bsrc[8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = (tid >> 3) + 32 * i;
-      asrc[i] = p.A + (row0 + min(r, rows_valid - 1)) * lda + cch * 16;
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int r = (tid >> 3) + 32 * i;
-      const int h = r >> 7;
-      const int rr = r & 127;
-      const int wrow = (h && half1) ? n0 + p.half_stride + rr : n0 + rr;
-      bsrc[i] = Wexp + static_cast<int64_t>(wrow) * lda + cch * 16;
-    }
-    const float* assrc = nullptr;
-    if constexpr (DT == DT_FP8)
-      assrc = p.As + (row0 + min(tid & (BM - 1), rows_valid - 1)) * kgroups;
-    const float* wsb0 = nullptr;
-    const float* wsb1 = nullptr;
-    if constexpr (DT == DT_FP8) {
+    // Buffer resources: A over the whole expert-major buffer, W over this
+    // expert's [N, K] block.  Rows past the end of a resource read as 0, so
+    // a tail tile may read past its expert's last row without a clamp; those
+    // rows are never stored.
+    const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(p.A), 0, static_cast<int>(p.rows_cap * lda), kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rW = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(p.W + static_cast<int64_t>(e) * p.N * lda), 0,
+        static_cast<int>(p.N * lda), kRsrcWord3);
+    // this wave stages A rows 16*wave + [0,16) and W-tile rows 32*wave + [0,32)
+    // (waves 0-3: half 0, waves 4-7: half 1)
+    const int a_row_off = static_cast<int>((row0 + 16 * wave) * lda);
+    const int w_row = n0 + (wave >> 2) * (half1 ? p.half_stride : 0) + 32 * (wave & 3);
+    const int w_row_off = static_cast<int>(w_row * lda);
+    __amdgpu_buffer_rsrc_t rS = rA;              // FP8: the A-scale buffer
+    int s_row_off = 0;
+    float vsw[2][2] = {{0.f, 0.f}, {0.f, 0.f}};   // weight scales of the tile, lane g = group g
+    if constexpr (kFp8) {
+      rS = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(p.As), 0,
+                                             static_cast<int>(p.rows_cap * kgroups * 4), kRsrcWord3);
+      s_row_off = static_cast<int>((row0 + 16 * wave) * kgroups * 4);
       const float* wse = p.Ws + static_cast<int64_t>(e) * (p.N / 128) * kgroups;
-      wsb0 = wse + static_cast<int64_t>(n0 / 128) * kgroups;
-      wsb1 = wse + static_cast<int64_t>((half1 ? n0 + p.half_stride : n0) / 128) * kgroups;
+      const float* w0 = wse + static_cast<int64_t>(n0 / 128) * kgroups;
+      const float* w1 = wse + static_cast<int64_t>((half1 ? n0 + p.half_stride : n0) / 128) * kgroups;
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int g = lane + 64 * q;
+        vsw[0][q] = g < kgroups ? w0[g] : 0.f;
+        vsw[1][q] = g < kgroups ? w1[g] : 0.f;
+      }
+      // these loads must not be in flight once the staged loads start
+      __builtin_amdgcn_s_waitcnt(VmCnt<0>::imm);
     }
 
-    u4 ra[4], rb[8];
-    float ras = 0.f;
-    auto fetch = [&](int ks) {
+    // issue the direct-to-LDS loads of K stage ks into ring slot s
+    auto issue = [&](int s, int ks) {
+      uint8_t* st = s_ring + s * STAGE;
+      typedef __attribute__((address_space(3))) void* lds_void;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) ra[i] = *reinterpret_cast<const u4*>(asrc[i] + ks * KB);
+      for (int j = 0; j < 2; ++j)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rA, (lds_void)(st + (16 * wave + 8 * j) * KB), 16, j ? voff_o : voff_e,
+            a_row_off + static_cast<int>(8 * j * lda) + ks * KB, 0, 0);
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        rb[i] = __builtin_nontemporal_load(reinterpret_cast<const u4*>(bsrc[i] + ks * KB));
-      if constexpr (DT == DT_FP8) {
-        if (tid < BM) ras = assrc[ks];
-      }
-    };
-    auto commit = [&](int s) {
-      Stage& st = sm.st[s];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        *reinterpret_cast<u4*>(st.a + swz((tid >> 3) + 32 * i, cch)) = ra[i];
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        *reinterpret_cast<u4*>(st.b + swz((tid >> 3) + 32 * i, cch)) = rb[i];
-      if constexpr (DT == DT_FP8) {
-        if (tid < BM) st.as[tid] = ras;
+      for (int j = 0; j < 4; ++j)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rW, (lds_void)(st + A_BYTES + (32 * wave + 8 * j) * KB), 16, (j & 1) ? voff_o : voff_e,
+            w_row_off + static_cast<int>(8 * j * lda) + ks * KB, 0, 0);
+      if constexpr (kFp8) {
+        if (lane < 16)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              rS, (lds_void)(st + A_BYTES + B_BYTES + 16 * wave * 4), 4, soff, s_row_off + ks * 4, 0, 0);
       }
     };
 
-    v4f acc[4][2][4];
+    v4f acc[4][2][2];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][h][j] = v4f{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < 2; ++j) acc[i][h][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    __syncthreads();               // previous tile's readers of stage 0 are done
-    fetch(0);
-    commit(0);
+    __syncthreads();               // every wave is done with the ring of the previous tile
+    issue(0, 0);
+    if (kstages > 1) issue(1, 1);
     for (int ks = 0; ks < kstages; ++ks) {
-      __syncthreads();             // stage ks&1 complete; stage (ks+1)&1 free
-      const bool more = ks + 1 < kstages;
-      if (more) fetch(ks + 1);
-      const Stage& st = sm.st[ks & 1];
-      u4 alo[4], ahi[4];
+      // this wave's loads of stage ks have landed (those of ks+1 may not)
+      if (ks + 1 < kstages)
+        __builtin_amdgcn_s_waitcnt(VmCnt<NLOAD>::imm);
+      else
+        __builtin_amdgcn_s_waitcnt(VmCnt<0>::imm);
+      __builtin_amdgcn_s_barrier();          // ... and every other wave's; slot (ks+2)%3 is free
+      if (ks + 2 < kstages) issue((ks + 2) % NST, ks + 2);
+
+      const uint32_t sb = ring + (ks % NST) * STAGE;
+      const uint32_t a0 = sb + (wm * 64 + frow) * KB + fc0;
+      const uint32_t a1 = sb + (wm * 64 + frow) * KB + fc1;
+      const uint32_t b0 = sb + A_BYTES + (wn * 32 + frow) * KB + fc0;
+      const uint32_t b1 = sb + A_BYTES + (wn * 32 + frow) * KB + fc1;
+      u4 af[8], bf[8];
+      // A fragments of the 4 row sub-tiles; B fragments (half, 16-col sub-tile)
+      // at (0,0) (0,1) (1,0) (1,1)
+      MOE_DS8(af, a0, a1, 0, 2048, 4096, 6144);
+      MOE_DS8(bf, b0, b1, 0, 2048, 16384, 18432);
+      if constexpr (kFp8) {
+        u4 sv[4];
+        const uint32_t s0 = sb + A_BYTES + B_BYTES + (wm * 64 + (lane >> 4) * 4) * 4;
+        MOE_DS4(sv, s0, 0, 64, 128, 192);
+        const int q = ks >> 6;
+        float sw[2];
+        sw[0] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+            __builtin_bit_cast(int, q ? vsw[0][1] : vsw[0][0]), ks & 63));
+        sw[1] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+            __builtin_bit_cast(int, q ? vsw[1][1] : vsw[1][0]), ks & 63));
+        // the 16 products of this stage first (independent: the matrix core
+        // runs them back to back), then the scaled fp32 accumulation
+        v4f pp[4][2][2];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) frag(st.a, wm * 64 + i * 16 + (lane & 15), lane >> 4, alo[i], ahi[i]);
-      float sa[4][4];
-      float sw[2] = {1.f, 1.f};
-      if constexpr (DT == DT_FP8) {
-        const int g = ks;                  // one stage == one scale group
-        sw[0] = wsb0[g];
-        sw[1] = wsb1[g];
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float4 v = *reinterpret_cast<const float4*>(&st.as[wm * 64 + i * 16 + (lane >> 4) * 4]);
-          sa[i][0] = v.x; sa[i][1] = v.y; sa[i][2] = v.z; sa[i][3] = v.w;
-        }
-      }
+          for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        u4 blo[4], bhi[4];
+            for (int i = 0; i < 4; ++i)
+              pp[i][h][j] = mma_stage<DT>(af[2 * i], af[2 * i + 1], bf[4 * h + 2 * j],
+                                          bf[4 * h + 2 * j + 1], v4f{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          frag(st.b, h * BH + wn * 64 + j * 16 + (lane & 15), lane >> 4, blo[j], bhi[j]);
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          if constexpr (DT == DT_FP8) {
-            float f[4];
+          for (int h = 0; h < 2; ++h)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) f[r] = sa[i][r] * sw[h];
+            for (int r = 0; r < 4; ++r) {
+              const float f = __uint_as_float(sv[i][r]) * sw[h];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const v4f pj = mma_stage<DT>(alo[i], ahi[i], blo[j], bhi[j], v4f{0.f, 0.f, 0.f, 0.f});
-#pragma unroll
-              for (int r = 0; r < 4; ++r) acc[i][h][j][r] = fmaf(pj[r], f[r], acc[i][h][j][r]);
+              for (int j = 0; j < 2; ++j) acc[i][h][j][r] = fmaf(pp[i][h][j][r], f, acc[i][h][j][r]);
             }
-          } else {
+      } else {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) acc[i][h][j] = mma_stage<DT>(alo[i], ahi[i], blo[j], bhi[j], acc[i][h][j]);
-          }
-        }
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              acc[i][h][j] = mma_stage<DT>(af[2 * i], af[2 * i + 1], bf[4 * h + 2 * j],
+                                           bf[4 * h + 2 * j + 1], acc[i][h][j]);
       }
-      if (more) commit((ks + 1) & 1);
     }
 
-    // ---- epilogue.  Lane holds rows i*16 + (lane>>4)*4 + r, column j*16 + (lane&15).
+    // ---- epilogue.  Lane holds rows i*16 + (lane>>4)*4 + r, columns
+    // j*16 + (lane&15) of its 32-column slice of each half.
     const int rbase = wm * 64 + (lane >> 4) * 4;
-    const int cbase = wn * 64 + (lane & 15);
+    const int cbase = wn * 32 + (lane & 15);
     if constexpr (EPI == EPI_STORE_F32 || EPI == EPI_STORE_BF16) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
@@ -336,7 +407,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs p) {
             if (row >= rows_valid) continue;
             const int64_t o = (row0 + row) * p.ldo + ncol0;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
+            for (int j = 0; j < 2; ++j) {
               const int c = cbase + j * 16;
               if constexpr (EPI == EPI_STORE_F32)
                 static_cast<float*>(p.out)[o + c] = acc[i][h][j][r];
@@ -347,25 +418,23 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs p) {
       }
     } else {
       // Z = SiLU(gate) * up, columns nb*128 + [0,128) of Z
-      float z[4][4][4];
+      float z[4][2][4];
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 2; ++j)
 #pragma unroll
           for (int r = 0; r < 4; ++r) z[i][j][r] = moe::silu(acc[i][0][j][r]) * acc[i][1][j][r];
       const int64_t zcol0 = static_cast<int64_t>(nb) * BH;
       if constexpr (EPI == EPI_SILU_FP8) {
-        // per-row amax over the 128 Z columns: 4 in-lane, 16 lanes, 2 waves
+        // per-row amax over the 128 Z columns: 2 in-lane, 16 lanes, 4 waves
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            float m = 0.f;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) m = fmaxf(m, fabsf(z[i][j][r]));
+            float m = fmaxf(fabsf(z[i][0][r]), fabsf(z[i][1][r]));
             m = moe::group16_max(m);
-            if ((lane & 15) == 0) sm.amax[wn][rbase + i * 16 + r] = m;
+            if ((lane & 15) == 0) s_amax[wn][rbase + i * 16 + r] = m;
           }
         __syncthreads();
 #pragma unroll
@@ -373,12 +442,13 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs p) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int row = rbase + i * 16 + r;
-            const float amax = moe::fp8_group_amax_clamp(fmaxf(sm.amax[0][row], sm.amax[1][row]));
+            const float amax = moe::fp8_group_amax_clamp(
+                fmaxf(fmaxf(s_amax[0][row], s_amax[1][row]), fmaxf(s_amax[2][row], s_amax[3][row])));
             const float inv = moe::fp8_group_inv(amax);
             if (row >= rows_valid) continue;
             uint8_t* zrow = static_cast<uint8_t*>(p.out) + (row0 + row) * p.ldo + zcol0;
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < 2; ++j)
               zrow[cbase + j * 16] = static_cast<uint8_t>(moe::f32x2_to_e4m3(z[i][j][r] * inv, 0.f));
             if (wn == 0 && (lane & 15) == 0)
               p.out_scales[(row0 + row) * (p.ldo / 128) + nb] = moe::fp8_group_scale(amax);
@@ -392,7 +462,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs p) {
             if (row >= rows_valid) continue;
             const int64_t o = (row0 + row) * p.ldo + zcol0;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
+            for (int j = 0; j < 2; ++j) {
               if constexpr (EPI == EPI_SILU_F32)
                 static_cast<float*>(p.out)[o + cbase + j * 16] = z[i][j][r];
               else
@@ -411,15 +481,7 @@ moe_status launch(const GemmArgs& a, int max_mtiles, hipStream_t stream) {
   const int cus = moe_host::device_cu_count();
   int grid = static_cast<int>(std::min<int64_t>(max_tiles, cus));
   if (grid >= 8) grid &= ~7;
-  const size_t smem = sizeof(Smem);
-  static bool attr_set = false;   // one kernel instance per template pair
-  if (!attr_set) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&grouped_gemm_kernel<DT, EPI>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem)) != hipSuccess)
-      return MOE_ERR_HIP;
-    attr_set = true;
-  }
-  grouped_gemm_kernel<DT, EPI><<<grid, kThreads, smem, stream>>>(a);
+  grouped_gemm_kernel<DT, EPI><<<grid, kThreads, 0, stream>>>(a);
   MOE_LAUNCH_CHECK();
   return MOE_OK;
 }
@@ -439,6 +501,13 @@ int max_row_tiles(int64_t rows_cap, int L) {
   return static_cast<int>(std::min<int64_t>(rows_cap / BM + L, (rows_cap + BM - 1) / BM + L));
 }
 
+// Staged loads address A and one expert's W through 32-bit buffer
+// resources with signed 32-bit offsets: both must span less than 2 GiB.
+bool offsets_fit(int64_t K_bytes, int64_t N, int64_t rows_cap) {
+  const int64_t lim = int64_t(1) << 31;
+  return K_bytes * N < lim && K_bytes * (rows_cap + BM) < lim;
+}
+
 }  // namespace
 
 extern "C" moe_status moe_grouped_gemm_w13(const void* a, moe_dtype a_dt, const float* a_scales,
@@ -454,6 +523,10 @@ extern "C" moe_status moe_grouped_gemm_w13(const void* a, moe_dtype a_dt, const 
   MOE_CHECK(a_dt == w_dt, MOE_ERR_UNSUPPORTED);
   MOE_CHECK(H % 128 == 0 && I % 128 == 0, MOE_ERR_UNSUPPORTED);
   MOE_CHECK(epi == MOE_EPI_SILU_MUL || out_dt == MOE_F32, MOE_ERR_UNSUPPORTED);
+  MOE_CHECK(offsets_fit(static_cast<int64_t>(H) * moe_host::elem_bytes(a_dt), 2 * static_cast<int64_t>(I),
+                        rows_cap),
+            MOE_ERR_UNSUPPORTED);
+  MOE_CHECK(a_dt != MOE_FP8_E4M3 || H <= 128 * 128, MOE_ERR_UNSUPPORTED);
   if (rows_cap == 0) return MOE_OK;
   MOE_CHECK(a && w13 && counts && offsets && out, MOE_ERR_INVALID_ARG);
   MOE_CHECK(a_dt != MOE_FP8_E4M3 || (a_scales && w13_scales), MOE_ERR_INVALID_ARG);
@@ -498,6 +571,9 @@ extern "C" moe_status moe_grouped_gemm_w2(const void* z, moe_dtype z_dt, const f
   MOE_CHECK(z_dt == w_dt, MOE_ERR_UNSUPPORTED);
   MOE_CHECK(H % 128 == 0 && I % 128 == 0, MOE_ERR_UNSUPPORTED);
   MOE_CHECK(out_dt == MOE_F32 || out_dt == MOE_BF16, MOE_ERR_UNSUPPORTED);
+  MOE_CHECK(offsets_fit(static_cast<int64_t>(I) * moe_host::elem_bytes(z_dt), H, rows_cap),
+            MOE_ERR_UNSUPPORTED);
+  MOE_CHECK(z_dt != MOE_FP8_E4M3 || I <= 128 * 128, MOE_ERR_UNSUPPORTED);
   if (rows_cap == 0) return MOE_OK;
   MOE_CHECK(z && w2 && counts && offsets && out, MOE_ERR_INVALID_ARG);
   MOE_CHECK(z_dt != MOE_FP8_E4M3 || (z_scales && w2_scales), MOE_ERR_INVALID_ARG);
