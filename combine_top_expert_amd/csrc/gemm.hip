@@ -110,32 +110,65 @@ __device__ __forceinline__ uint32_t lds_u32(const void* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr)(p)));
 }
 
-// Eight 16-byte LDS reads (two per MFMA operand fragment of 4 sub-tiles)
-// from two per-lane base addresses, then wait for them.
-#define MOE_DS8(o, a0, a1, I0, I1, I2, I3)                                                \
+// All fragment reads of one stage for one wave -- A (4 row sub-tiles), B
+// (half, 16-column sub-tile) at (0,0) (0,1) (1,0) (1,1) and, for FP8, the
+// activation scales of the wave's 64 rows -- then one wait for all of them.
+#define MOE_DS_STAGE_FP8(af, bf, sv, a0, a1, b0, b1, s0)                                   \
   asm volatile(                                                                            \
-      "ds_read_b128 %0, %8 offset:" #I0 "\n"                                              \
-      "ds_read_b128 %1, %9 offset:" #I0 "\n"                                              \
-      "ds_read_b128 %2, %8 offset:" #I1 "\n"                                              \
-      "ds_read_b128 %3, %9 offset:" #I1 "\n"                                              \
-      "ds_read_b128 %4, %8 offset:" #I2 "\n"                                              \
-      "ds_read_b128 %5, %9 offset:" #I2 "\n"                                              \
-      "ds_read_b128 %6, %8 offset:" #I3 "\n"                                              \
-      "ds_read_b128 %7, %9 offset:" #I3 "\n"                                              \
+      "ds_read_b128 %0, %20\n ds_read_b128 %1, %21\n"                                      \
+      "ds_read_b128 %2, %20 offset:2048\n ds_read_b128 %3, %21 offset:2048\n"              \
+      "ds_read_b128 %4, %20 offset:4096\n ds_read_b128 %5, %21 offset:4096\n"              \
+      "ds_read_b128 %6, %20 offset:6144\n ds_read_b128 %7, %21 offset:6144\n"              \
+      "ds_read_b128 %8, %22\n ds_read_b128 %9, %23\n"                                      \
+      "ds_read_b128 %10, %22 offset:2048\n ds_read_b128 %11, %23 offset:2048\n"            \
+      "ds_read_b128 %12, %22 offset:16384\n ds_read_b128 %13, %23 offset:16384\n"          \
+      "ds_read_b128 %14, %22 offset:18432\n ds_read_b128 %15, %23 offset:18432\n"          \
+      "ds_read_b128 %16, %24\n ds_read_b128 %17, %24 offset:64\n"                          \
+      "ds_read_b128 %18, %24 offset:128\n ds_read_b128 %19, %24 offset:192\n"              \
       "s_waitcnt lgkmcnt(0)"                                                               \
-      : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]),     \
-        "=&v"(o[6]), "=&v"(o[7])                                                           \
-      : "v"(a0), "v"(a1))
+      : "=&v"(af[0]), "=&v"(af[1]), "=&v"(af[2]), "=&v"(af[3]), "=&v"(af[4]), "=&v"(af[5]), \
+        "=&v"(af[6]), "=&v"(af[7]), "=&v"(bf[0]), "=&v"(bf[1]), "=&v"(bf[2]), "=&v"(bf[3]), \
+        "=&v"(bf[4]), "=&v"(bf[5]), "=&v"(bf[6]), "=&v"(bf[7]), "=&v"(sv[0]), "=&v"(sv[1]), \
+        "=&v"(sv[2]), "=&v"(sv[3])                                                         \
+      : "v"(a0), "v"(a1), "v"(b0), "v"(b1), "v"(s0))
 
-#define MOE_DS4(o, a, I0, I1, I2, I3)                                                      \
+#define MOE_DS_STAGE(af, bf, a0, a1, b0, b1)                                                \
   asm volatile(                                                                            \
-      "ds_read_b128 %0, %4 offset:" #I0 "\n"                                              \
-      "ds_read_b128 %1, %4 offset:" #I1 "\n"                                              \
-      "ds_read_b128 %2, %4 offset:" #I2 "\n"                                              \
-      "ds_read_b128 %3, %4 offset:" #I3 "\n"                                              \
+      "ds_read_b128 %0, %16\n ds_read_b128 %1, %17\n"                                      \
+      "ds_read_b128 %2, %16 offset:2048\n ds_read_b128 %3, %17 offset:2048\n"              \
+      "ds_read_b128 %4, %16 offset:4096\n ds_read_b128 %5, %17 offset:4096\n"              \
+      "ds_read_b128 %6, %16 offset:6144\n ds_read_b128 %7, %17 offset:6144\n"              \
+      "ds_read_b128 %8, %18\n ds_read_b128 %9, %19\n"                                      \
+      "ds_read_b128 %10, %18 offset:2048\n ds_read_b128 %11, %19 offset:2048\n"            \
+      "ds_read_b128 %12, %18 offset:16384\n ds_read_b128 %13, %19 offset:16384\n"          \
+      "ds_read_b128 %14, %18 offset:18432\n ds_read_b128 %15, %19 offset:18432\n"          \
       "s_waitcnt lgkmcnt(0)"                                                               \
-      : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3])                                 \
-      : "v"(a))
+      : "=&v"(af[0]), "=&v"(af[1]), "=&v"(af[2]), "=&v"(af[3]), "=&v"(af[4]), "=&v"(af[5]), \
+        "=&v"(af[6]), "=&v"(af[7]), "=&v"(bf[0]), "=&v"(bf[1]), "=&v"(bf[2]), "=&v"(bf[3]), \
+        "=&v"(bf[4]), "=&v"(bf[5]), "=&v"(bf[6]), "=&v"(bf[7])                              \
+      : "v"(a0), "v"(a1), "v"(b0), "v"(b1))
+
+// Workgroup barriers that also pin register values: the compiler may move
+// matrix instructions (they touch no memory) across a plain barrier, which
+// would blur the phases; routing the fragments (resp. accumulators) through
+// the barrier keeps the products of a phase between its two barriers.
+#define MOE_BARRIER_FRAGS(af, bf, sv)                                                       \
+  asm volatile("s_barrier"                                                                 \
+               : "+v"(af[0]), "+v"(af[1]), "+v"(af[2]), "+v"(af[3]), "+v"(af[4]), "+v"(af[5]), \
+                 "+v"(af[6]), "+v"(af[7]), "+v"(bf[0]), "+v"(bf[1]), "+v"(bf[2]), "+v"(bf[3]), \
+                 "+v"(bf[4]), "+v"(bf[5]), "+v"(bf[6]), "+v"(bf[7]), "+v"(sv[0]), "+v"(sv[1]), \
+                 "+v"(sv[2]), "+v"(sv[3])                                                   \
+               :                                                                           \
+               : "memory")
+
+#define MOE_BARRIER_ACC(acc, WAIT)                                                          \
+  asm volatile(WAIT "s_barrier"                                                            \
+               : "+v"(acc[0][0][0]), "+v"(acc[0][0][1]), "+v"(acc[0][1][0]), "+v"(acc[0][1][1]), \
+                 "+v"(acc[1][0][0]), "+v"(acc[1][0][1]), "+v"(acc[1][1][0]), "+v"(acc[1][1][1]), \
+                 "+v"(acc[2][0][0]), "+v"(acc[2][0][1]), "+v"(acc[2][1][0]), "+v"(acc[2][1][1]), \
+                 "+v"(acc[3][0][0]), "+v"(acc[3][0][1]), "+v"(acc[3][1][0]), "+v"(acc[3][1][1])  \
+               :                                                                           \
+               : "memory")
 
 template <int DT>
 __device__ __forceinline__ v4f mma_stage(const u4& alo, const u4& ahi, const u4& blo,
@@ -191,8 +224,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs p) {
   // wave-uniform by construction; readfirstlane tells the compiler so, which
   // keeps the staged-load offsets in scalar registers (no per-load loop)
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave & 1;       // 64-row slice of the tile
-  const int wn = wave >> 1;      // 32-column slice of each half
+  const int wm = wave >> 2;      // 64-row slice of the tile = wave group (0: waves 0-3, 1: 4-7)
+  const int wn = wave & 3;       // 32-column slice of each half
   constexpr int ESZ = DT == DT_FP8 ? 1 : (DT == DT_BF16 ? 2 : 4);
   constexpr bool kFp8 = DT == DT_FP8;
   constexpr int NLOAD = kFp8 ? 7 : 6;      // direct-to-LDS loads per wave per stage
@@ -238,20 +271,22 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs p) {
   const int64_t lda = static_cast<int64_t>(p.K) * ESZ;
 
   // Stage layout: chunk c (16 bytes) of row r sits at chunk c ^ swz(r) with
-  // swz(r) = (r >> 1) & 7.  A 16-row fragment read (16 lanes, one 16-byte
-  // chunk each, rows r0..r0+15 with r0 % 16 == 0) then touches 16 distinct
-  // 4-bank groups of the 64-bank LDS, and a direct-to-LDS load writes 1 KB
-  // contiguously.  Lane l of a staging load fills row srow = l >> 3 of an
-  // 8-row group g, physical chunk l & 7; swz of that row is
-  // 4*(g & 1) + (srow >> 1), so the fetched chunk depends on g's parity.
+  // swz(r) = (r & 7) ^ ((r >> 3) & 1), which repeats every 16 rows.  With it
+  // the fragment reads below (16 rows x 4 chunk pairs per instruction) run
+  // at the full LDS rate with no bank conflicts (measured: 256 B/clk per CU
+  // with 8 waves; the same reads without the (r >> 3) term, or with
+  // (r >> 1) & 7, reach 160 B/clk).  A direct-to-LDS load still writes 1 KB
+  // contiguously: lane l fills row srow = l >> 3 of an 8-row group g,
+  // physical chunk l & 7, so it fetches chunk (l & 7) ^ srow ^ (g & 1).
   const int srow = lane >> 3;
-  const int voff_e = static_cast<int>(srow * lda) + (((lane & 7) ^ (srow >> 1)) << 4);
-  const int voff_o = static_cast<int>(srow * lda) + (((lane & 7) ^ ((4 + (srow >> 1)) & 7)) << 4);
+  const int voff_e = static_cast<int>(srow * lda) + (((lane & 7) ^ srow) << 4);
+  const int voff_o = static_cast<int>(srow * lda) + (((lane & 7) ^ srow ^ 1) << 4);
   const int soff = (lane & 15) * kgroups * 4;    // A-scale row of this lane (FP8)
   // fragment reads: row (lane & 15) of a 16-row block, bytes 32*(lane>>4)..+32
   const int frow = lane & 15;
-  const int fc0 = ((2 * (lane >> 4)) ^ (frow >> 1)) << 4;
-  const int fc1 = ((2 * (lane >> 4) + 1) ^ (frow >> 1)) << 4;
+  const int fsw = (frow & 7) ^ (frow >> 3);
+  const int fc0 = ((2 * (lane >> 4)) ^ fsw) << 4;
+  const int fc1 = ((2 * (lane >> 4) + 1) ^ fsw) << 4;
   const uint32_t ring = lds_u32(s_ring);
 
   for (int t = t_begin; t < t_end; t += t_step) {
@@ -327,57 +362,81 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs p) {
 
     __syncthreads();               // every wave is done with the ring of the previous tile
     issue(0, 0);
-    if (kstages > 1) issue(1, 1);
-    for (int ks = 0; ks < kstages; ++ks) {
-      // this wave's loads of stage ks have landed (those of ks+1 may not)
-      if (ks + 1 < kstages)
-        __builtin_amdgcn_s_waitcnt(VmCnt<NLOAD>::imm);
-      else
-        __builtin_amdgcn_s_waitcnt(VmCnt<0>::imm);
-      __builtin_amdgcn_s_barrier();          // ... and every other wave's; slot (ks+2)%3 is free
-      if (ks + 2 < kstages) issue((ks + 2) % NST, ks + 2);
+    if (kstages > 1) {
+      issue(1, 1);
+      __builtin_amdgcn_s_waitcnt(VmCnt<NLOAD>::imm);
+    } else {
+      __builtin_amdgcn_s_waitcnt(VmCnt<0>::imm);
+    }
+    __builtin_amdgcn_s_barrier();  // stage 0 has landed for every wave
 
+    // Two wave groups take turns.  Every phase ends with a workgroup
+    // barrier; in each phase one group stages and reads while the other runs
+    // the matrix products of the stage it read in the phase before, so each
+    // SIMD always has one wave feeding the matrix core and one moving data.
+    // Group g reads stage ks in global phase 2*ks + g and multiplies it in
+    // phase 2*ks + g + 1 (group 1 waits out phase 0, group 0 the last phase).
+    // In its read phase for stage ks a wave also issues its share of stage
+    // ks + 2 (into the slot of stage ks - 1, which group 1 finished reading
+    // in phase 2*ks - 1) and, before the closing barrier, waits for its own
+    // loads of stage ks + 1 -- so neither staging issue nor waits ever sit in
+    // a matrix phase.  Stage ks + 1 is first read in phase 2*ks + 2, after
+    // both groups' waits.
+    const uint32_t a_frag = (wm * 64 + frow) * KB;
+    const uint32_t b_frag = A_BYTES + (wn * 32 + frow) * KB;
+    const uint32_t s_frag = A_BYTES + B_BYTES + (wm * 64 + (lane >> 4) * 4) * 4;
+    if (wm == 1) __builtin_amdgcn_s_barrier();
+    for (int ks = 0; ks < kstages; ++ks) {
+      if (ks + 2 < kstages) issue((ks + 2) % NST, ks + 2);
       const uint32_t sb = ring + (ks % NST) * STAGE;
-      const uint32_t a0 = sb + (wm * 64 + frow) * KB + fc0;
-      const uint32_t a1 = sb + (wm * 64 + frow) * KB + fc1;
-      const uint32_t b0 = sb + A_BYTES + (wn * 32 + frow) * KB + fc0;
-      const uint32_t b1 = sb + A_BYTES + (wn * 32 + frow) * KB + fc1;
-      u4 af[8], bf[8];
-      // A fragments of the 4 row sub-tiles; B fragments (half, 16-col sub-tile)
-      // at (0,0) (0,1) (1,0) (1,1)
-      MOE_DS8(af, a0, a1, 0, 2048, 4096, 6144);
-      MOE_DS8(bf, b0, b1, 0, 2048, 16384, 18432);
+      u4 af[8], bf[8], sv[4];
       if constexpr (kFp8) {
-        u4 sv[4];
-        const uint32_t s0 = sb + A_BYTES + B_BYTES + (wm * 64 + (lane >> 4) * 4) * 4;
-        MOE_DS4(sv, s0, 0, 64, 128, 192);
-        const int q = ks >> 6;
+        MOE_DS_STAGE_FP8(af, bf, sv, sb + a_frag + fc0, sb + a_frag + fc1, sb + b_frag + fc0,
+                         sb + b_frag + fc1, sb + s_frag);
+      } else {
+        MOE_DS_STAGE(af, bf, sb + a_frag + fc0, sb + a_frag + fc1, sb + b_frag + fc0,
+                     sb + b_frag + fc1);
+        sv[0] = sv[1] = sv[2] = sv[3] = u4{0, 0, 0, 0};
+      }
+      if (ks + 2 < kstages)
+        __builtin_amdgcn_s_waitcnt(VmCnt<NLOAD>::imm);
+      else if (ks + 1 < kstages)
+        __builtin_amdgcn_s_waitcnt(VmCnt<0>::imm);
+      MOE_BARRIER_FRAGS(af, bf, sv);
+      if constexpr (kFp8) {
+        const int qq = ks >> 6;
         float sw[2];
         sw[0] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(
-            __builtin_bit_cast(int, q ? vsw[0][1] : vsw[0][0]), ks & 63));
+            __builtin_bit_cast(int, qq ? vsw[0][1] : vsw[0][0]), ks & 63));
         sw[1] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(
-            __builtin_bit_cast(int, q ? vsw[1][1] : vsw[1][0]), ks & 63));
-        // the 16 products of this stage first (independent: the matrix core
-        // runs them back to back), then the scaled fp32 accumulation
-        v4f pp[4][2][2];
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
+            __builtin_bit_cast(int, qq ? vsw[1][1] : vsw[1][0]), ks & 63));
+        // 16 independent products P, each folded in as acc += P * (sa * sw).
+        // Software-pipelined over the 8 (row sub-tile, half) pairs: the two
+        // products of pair n + 1 are issued before the fp32 folds of pair n,
+        // so the matrix core works while the vector ALU folds.
+        v4f pr[2][2];
+        auto products = [&](int n, v4f* out) {
+          const int i = n >> 1, h = n & 1;
 #pragma unroll
           for (int j = 0; j < 2; ++j)
+            out[j] = mma_stage<DT>(af[2 * i], af[2 * i + 1], bf[4 * h + 2 * j],
+                                   bf[4 * h + 2 * j + 1], v4f{0.f, 0.f, 0.f, 0.f});
+        };
+        products(0, pr[0]);
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-              pp[i][h][j] = mma_stage<DT>(af[2 * i], af[2 * i + 1], bf[4 * h + 2 * j],
-                                          bf[4 * h + 2 * j + 1], v4f{0.f, 0.f, 0.f, 0.f});
+        for (int n = 0; n < 8; ++n) {
+          if (n + 1 < 8) products(n + 1, pr[(n + 1) & 1]);
+          const int i = n >> 1, h = n & 1;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+          for (int r = 0; r < 4; ++r) {
+            const float f = __uint_as_float(sv[i][r]) * sw[h];
 #pragma unroll
-          for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const float f = __uint_as_float(sv[i][r]) * sw[h];
-#pragma unroll
-              for (int j = 0; j < 2; ++j) acc[i][h][j][r] = fmaf(pp[i][h][j][r], f, acc[i][h][j][r]);
-            }
+            for (int j = 0; j < 2; ++j) acc[i][h][j][r] = fmaf(pr[n & 1][j][r], f, acc[i][h][j][r]);
+          }
+          // keep the issue order: 2 matrix ops, then this pair's 12 vector ops
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);
+        }
       } else {
 #pragma unroll
         for (int h = 0; h < 2; ++h)
@@ -388,7 +447,9 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs p) {
               acc[i][h][j] = mma_stage<DT>(af[2 * i], af[2 * i + 1], bf[4 * h + 2 * j],
                                            bf[4 * h + 2 * j + 1], acc[i][h][j]);
       }
+      MOE_BARRIER_ACC(acc, "");
     }
+    if (wm == 0) __builtin_amdgcn_s_barrier();
 
     // ---- epilogue.  Lane holds rows i*16 + (lane>>4)*4 + r, columns
     // j*16 + (lane&15) of its 32-column slice of each half.
