@@ -110,29 +110,12 @@ __device__ __forceinline__ uint32_t lds_u32(const void* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr)(p)));
 }
 
-// All fragment reads of one stage for one wave -- A (4 row sub-tiles), B
-// (half, 16-column sub-tile) at (0,0) (0,1) (1,0) (1,1) and, for FP8, the
-// activation scales of the wave's 64 rows -- then one wait for all of them.
-#define MOE_DS_STAGE_FP8(af, bf, sv, a0, a1, b0, b1, s0)                                   \
-  asm volatile(                                                                            \
-      "ds_read_b128 %0, %20\n ds_read_b128 %1, %21\n"                                      \
-      "ds_read_b128 %2, %20 offset:2048\n ds_read_b128 %3, %21 offset:2048\n"              \
-      "ds_read_b128 %4, %20 offset:4096\n ds_read_b128 %5, %21 offset:4096\n"              \
-      "ds_read_b128 %6, %20 offset:6144\n ds_read_b128 %7, %21 offset:6144\n"              \
-      "ds_read_b128 %8, %22\n ds_read_b128 %9, %23\n"                                      \
-      "ds_read_b128 %10, %22 offset:2048\n ds_read_b128 %11, %23 offset:2048\n"            \
-      "ds_read_b128 %12, %22 offset:16384\n ds_read_b128 %13, %23 offset:16384\n"          \
-      "ds_read_b128 %14, %22 offset:18432\n ds_read_b128 %15, %23 offset:18432\n"          \
-      "ds_read_b128 %16, %24\n ds_read_b128 %17, %24 offset:64\n"                          \
-      "ds_read_b128 %18, %24 offset:128\n ds_read_b128 %19, %24 offset:192\n"              \
-      "s_waitcnt lgkmcnt(0)"                                                               \
-      : "=&v"(af[0]), "=&v"(af[1]), "=&v"(af[2]), "=&v"(af[3]), "=&v"(af[4]), "=&v"(af[5]), \
-        "=&v"(af[6]), "=&v"(af[7]), "=&v"(bf[0]), "=&v"(bf[1]), "=&v"(bf[2]), "=&v"(bf[3]), \
-        "=&v"(bf[4]), "=&v"(bf[5]), "=&v"(bf[6]), "=&v"(bf[7]), "=&v"(sv[0]), "=&v"(sv[1]), \
-        "=&v"(sv[2]), "=&v"(sv[3])                                                         \
-      : "v"(a0), "v"(a1), "v"(b0), "v"(b1), "v"(s0))
-
-#define MOE_DS_STAGE(af, bf, a0, a1, b0, b1)                                                \
+// Fragment reads of one stage for one wave, issued without waiting: A (4
+// row sub-tiles) and B (half, 16-column sub-tile) at (0,0) (0,1) (1,0)
+// (1,1); for FP8 the activation scales of the wave's 64 rows.  The
+// registers are only consumed after MOE_WAIT_BARRIER_FRAGS, which waits for
+// them (lgkmcnt) and carries them as operands.
+#define MOE_DS_AB(af, bf, a0, a1, b0, b1)                                                    \
   asm volatile(                                                                            \
       "ds_read_b128 %0, %16\n ds_read_b128 %1, %17\n"                                      \
       "ds_read_b128 %2, %16 offset:2048\n ds_read_b128 %3, %17 offset:2048\n"              \
@@ -141,19 +124,21 @@ __device__ __forceinline__ uint32_t lds_u32(const void* p) {
       "ds_read_b128 %8, %18\n ds_read_b128 %9, %19\n"                                      \
       "ds_read_b128 %10, %18 offset:2048\n ds_read_b128 %11, %19 offset:2048\n"            \
       "ds_read_b128 %12, %18 offset:16384\n ds_read_b128 %13, %19 offset:16384\n"          \
-      "ds_read_b128 %14, %18 offset:18432\n ds_read_b128 %15, %19 offset:18432\n"          \
-      "s_waitcnt lgkmcnt(0)"                                                               \
+      "ds_read_b128 %14, %18 offset:18432\n ds_read_b128 %15, %19 offset:18432"             \
       : "=&v"(af[0]), "=&v"(af[1]), "=&v"(af[2]), "=&v"(af[3]), "=&v"(af[4]), "=&v"(af[5]), \
         "=&v"(af[6]), "=&v"(af[7]), "=&v"(bf[0]), "=&v"(bf[1]), "=&v"(bf[2]), "=&v"(bf[3]), \
         "=&v"(bf[4]), "=&v"(bf[5]), "=&v"(bf[6]), "=&v"(bf[7])                              \
       : "v"(a0), "v"(a1), "v"(b0), "v"(b1))
 
-// Workgroup barriers that also pin register values: the compiler may move
-// matrix instructions (they touch no memory) across a plain barrier, which
-// would blur the phases; routing the fragments (resp. accumulators) through
-// the barrier keeps the products of a phase between its two barriers.
-#define MOE_BARRIER_FRAGS(af, bf, sv)                                                       \
-  asm volatile("s_barrier"                                                                 \
+#define MOE_DS_S(sv, s0)                                                                    \
+  asm volatile(                                                                            \
+      "ds_read_b128 %0, %4\n ds_read_b128 %1, %4 offset:64\n"                              \
+      "ds_read_b128 %2, %4 offset:128\n ds_read_b128 %3, %4 offset:192"                    \
+      : "=&v"(sv[0]), "=&v"(sv[1]), "=&v"(sv[2]), "=&v"(sv[3])                              \
+      : "v"(s0))
+
+#define MOE_WAIT_BARRIER_FRAGS(af, bf, sv)                                                  \
+  asm volatile("s_waitcnt lgkmcnt(0)\n s_barrier"                                          \
                : "+v"(af[0]), "+v"(af[1]), "+v"(af[2]), "+v"(af[3]), "+v"(af[4]), "+v"(af[5]), \
                  "+v"(af[6]), "+v"(af[7]), "+v"(bf[0]), "+v"(bf[1]), "+v"(bf[2]), "+v"(bf[3]), \
                  "+v"(bf[4]), "+v"(bf[5]), "+v"(bf[6]), "+v"(bf[7]), "+v"(sv[0]), "+v"(sv[1]), \
@@ -161,6 +146,19 @@ __device__ __forceinline__ uint32_t lds_u32(const void* p) {
                :                                                                           \
                : "memory")
 
+// Keeps the fp32 folds of a read phase before its closing barrier.
+#define MOE_PIN_ACC(acc)                                                                    \
+  asm volatile(""                                                                          \
+               : "+v"(acc[0][0][0]), "+v"(acc[0][0][1]), "+v"(acc[0][1][0]), "+v"(acc[0][1][1]), \
+                 "+v"(acc[1][0][0]), "+v"(acc[1][0][1]), "+v"(acc[1][1][0]), "+v"(acc[1][1][1]), \
+                 "+v"(acc[2][0][0]), "+v"(acc[2][0][1]), "+v"(acc[2][1][0]), "+v"(acc[2][1][1]), \
+                 "+v"(acc[3][0][0]), "+v"(acc[3][0][1]), "+v"(acc[3][1][0]), "+v"(acc[3][1][1])  \
+               :)
+
+// Workgroup barriers that also pin register values: the compiler may move
+// matrix instructions (they touch no memory) across a plain barrier, which
+// would blur the phases; routing the fragments (resp. accumulators) through
+// the barrier keeps the products of a phase between its two barriers.
 #define MOE_BARRIER_ACC(acc, WAIT)                                                          \
   asm volatile(WAIT "s_barrier"                                                            \
                : "+v"(acc[0][0][0]), "+v"(acc[0][0][1]), "+v"(acc[0][1][0]), "+v"(acc[0][1][1]), \
@@ -387,22 +385,23 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs p) {
     const uint32_t s_frag = A_BYTES + B_BYTES + (wm * 64 + (lane >> 4) * 4) * 4;
     if (wm == 1) __builtin_amdgcn_s_barrier();
     for (int ks = 0; ks < kstages; ++ks) {
-      if (ks + 2 < kstages) issue((ks + 2) % NST, ks + 2);
+      // fragment reads first (no wait), then the staging loads: a wave is
+      // held at a staging load until the memory pipeline takes it, and the
+      // reads complete meanwhile
       const uint32_t sb = ring + (ks % NST) * STAGE;
       u4 af[8], bf[8], sv[4];
+      MOE_DS_AB(af, bf, sb + a_frag + fc0, sb + a_frag + fc1, sb + b_frag + fc0, sb + b_frag + fc1);
       if constexpr (kFp8) {
-        MOE_DS_STAGE_FP8(af, bf, sv, sb + a_frag + fc0, sb + a_frag + fc1, sb + b_frag + fc0,
-                         sb + b_frag + fc1, sb + s_frag);
+        MOE_DS_S(sv, sb + s_frag);
       } else {
-        MOE_DS_STAGE(af, bf, sb + a_frag + fc0, sb + a_frag + fc1, sb + b_frag + fc0,
-                     sb + b_frag + fc1);
         sv[0] = sv[1] = sv[2] = sv[3] = u4{0, 0, 0, 0};
       }
+      if (ks + 2 < kstages) issue((ks + 2) % NST, ks + 2);
       if (ks + 2 < kstages)
         __builtin_amdgcn_s_waitcnt(VmCnt<NLOAD>::imm);
       else if (ks + 1 < kstages)
         __builtin_amdgcn_s_waitcnt(VmCnt<0>::imm);
-      MOE_BARRIER_FRAGS(af, bf, sv);
+      MOE_WAIT_BARRIER_FRAGS(af, bf, sv);
       if constexpr (kFp8) {
         const int qq = ks >> 6;
         float sw[2];
