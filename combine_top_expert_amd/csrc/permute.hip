@@ -2,9 +2,10 @@
 // block FP8 on the way ("SGLang、NCCL 与 MoE EP" §2.3.4 and §2.3.5;
 // "DeepEP 架构与实现笔记" §9.4 and §11).
 //
-// One wavefront per token.  The token's row is read from HBM once, in
-// 16-byte chunks per lane, quantised once (the code of a row does not depend
-// on which expert receives it), and stored to each of its local slots.  A
+// One wavefront per token.  The token's routes are read once (lane k =
+// route k); its row is read from HBM once, with up to 16 16-byte chunks per
+// lane in flight, quantised once (the code of a row does not depend on which
+// expert receives it), and stored to each of its local slots.  A
 // 128-column FP8 group is covered by 16 lanes (bf16 input) or 32 lanes
 // (fp32 input); its amax is a butterfly max inside those lanes.  Tokens
 // without a local route read nothing.
@@ -15,7 +16,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kTokPerBlock = kThreads / MOE_WAVE;
-constexpr int kUnroll = 4;
+constexpr int kUnroll = 16;          // 16-byte chunks per lane in flight (a 8192-column bf16 row)
 
 template <typename TIn> struct Vec;
 template <> struct Vec<uint16_t> {  // 8 bf16 per 16-byte chunk
@@ -56,13 +57,10 @@ __global__ __launch_bounds__(kThreads) void permute_kernel(const TIn* __restrict
   const int lane = moe::lane_id();
   const int t = blockIdx.x * kTokPerBlock + wave;
   if (t >= T) return;
-  const int32_t* so = slot_of + static_cast<int64_t>(t) * K;
-  bool any = false;
-  for (int k = 0; k < K; ++k) {
-    const int s = so[k];
-    any |= (s >= 0 && s < rows_cap);
-  }
-  if (!any) return;
+  // lane k holds route k of the token; ballot bit k marks a local slot
+  const int s_l = lane < K ? slot_of[static_cast<int64_t>(t) * K + lane] : -1;
+  const uint64_t routes = __ballot(s_l >= 0 && s_l < rows_cap);
+  if (!routes) return;
 
   const int nchunk = H / EPC;
   const uint4* xrow = reinterpret_cast<const uint4*>(x + static_cast<int64_t>(t) * H);
@@ -97,9 +95,9 @@ __global__ __launch_bounds__(kThreads) void permute_kernel(const TIn* __restrict
                                         f[4 * i + 3] * inv);
         const float scale = moe::fp8_group_scale(amax);
         const int g = c / LPG;
-        for (int k = 0; k < K; ++k) {
-          const int s = so[k];
-          if (s < 0 || s >= rows_cap || !live) continue;
+        for (uint64_t m = routes; m; m &= m - 1) {
+          const int s = __builtin_amdgcn_readlane(s_l, __builtin_ctzll(m));
+          if (!live) continue;
           uint8_t* dst = buf + static_cast<int64_t>(s) * out_row_bytes + c * EPC;
           if constexpr (EPC == 8) {
             *reinterpret_cast<uint2*>(dst) = make_uint2(codes[0], codes[1]);
@@ -109,9 +107,9 @@ __global__ __launch_bounds__(kThreads) void permute_kernel(const TIn* __restrict
           if ((lane % LPG) == 0) scales[static_cast<int64_t>(s) * groups + g] = scale;
         }
       } else {
-        for (int k = 0; k < K; ++k) {
-          const int s = so[k];
-          if (s < 0 || s >= rows_cap || !live) continue;
+        for (uint64_t m = routes; m; m &= m - 1) {
+          const int s = __builtin_amdgcn_readlane(s_l, __builtin_ctzll(m));
+          if (!live) continue;
           uint4* dst = reinterpret_cast<uint4*>(buf + static_cast<int64_t>(s) * out_row_bytes) + c;
           moe::store_nt16(dst, raw[u]);
         }
@@ -127,7 +125,7 @@ extern "C" moe_status moe_permute(const void* x, moe_dtype x_dt, int T, int K, i
                                   moe_dtype buf_dt, float* buf_scales, hipStream_t stream) {
   MOE_CHECK(T >= 0 && K > 0 && H > 0 && rows_cap >= 0, MOE_ERR_INVALID_ARG);
   MOE_CHECK(moe_host::valid_dtype(x_dt) && moe_host::valid_dtype(buf_dt), MOE_ERR_INVALID_ARG);
-  MOE_CHECK(H % 128 == 0, MOE_ERR_UNSUPPORTED);
+  MOE_CHECK(H % 128 == 0 && K <= 64, MOE_ERR_UNSUPPORTED);
   MOE_CHECK(x_dt == MOE_F32 || x_dt == MOE_BF16, MOE_ERR_UNSUPPORTED);
   MOE_CHECK(buf_dt == x_dt || buf_dt == MOE_FP8_E4M3, MOE_ERR_UNSUPPORTED);
   if (T == 0 || rows_cap == 0) return MOE_OK;

@@ -8,10 +8,12 @@
 //
 // combine: y[t] = sum_k w[t,k] * out[slot_of[t,k]] ("SGLang、NCCL 与 MoE EP"
 // §1.1 and §2.3.6; "DeepEP 架构与实现笔记" §9.4 combine_convert).  One
-// wavefront per token; every lane owns 8 consecutive columns per step and
-// has all K source rows of that step in flight at once.  Products and sums
-// are separate fp32 operations in k order (no fused multiply-add), so the
-// result equals a plain fp32 evaluation of the sum term by term.
+// wavefront per token.  The token's routes are read once (lane k = route k)
+// and its local routes walked in k order; for each, every lane has 8
+// 8-column chunks of the source row in flight at once (a whole 4096-column
+// bf16 row per wave per round trip).  Products and sums are separate fp32
+// operations in k order (no fused multiply-add), so the result equals a
+// plain fp32 evaluation of the sum term by term.
 
 #include "moe_common.h"
 
@@ -78,7 +80,7 @@ __global__ __launch_bounds__(kThreads) void silu_mul_kernel(const float* __restr
 }
 
 constexpr int kMaxK = 64;
-constexpr int kKU = 8;          // source rows in flight per lane
+constexpr int kCPL = 8;          // 8-column chunks per lane in flight per source row
 
 template <bool kInBf16, bool kOutBf16>
 __global__ __launch_bounds__(kThreads) void combine_kernel(const uint8_t* __restrict__ eo,
@@ -91,29 +93,35 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const uint8_t* __rest
   if (t >= T) return;
   constexpr int IB = kInBf16 ? 2 : 4;
   constexpr int OB = kOutBf16 ? 2 : 4;
-  const int32_t* so = slot_of + static_cast<int64_t>(t) * K;
-  const float* wt = w + static_cast<int64_t>(t) * K;
+  constexpr int NV = IB == 2 ? 1 : 2;            // 16-byte loads per 8-column chunk
+  // lane k holds route k of the token; the routes with a local row form a
+  // bit mask in k order (ballot bit k = lane k)
+  const int s_l = lane < K ? slot_of[static_cast<int64_t>(t) * K + lane] : -1;
+  const float w_l = lane < K ? w[static_cast<int64_t>(t) * K + lane] : 0.f;
+  const uint64_t routes = __ballot(s_l >= 0 && s_l < rows_cap);
   const int nchunk = H / 8;
-  for (int c = lane; c < nchunk; c += MOE_WAVE) {
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int k0 = 0; k0 < K; k0 += kKU) {
-      uint4 raw[kKU][IB == 2 ? 1 : 2];
-      bool ok[kKU];
+  uint8_t* yrow = y + static_cast<int64_t>(t) * H * OB;
+  for (int c0 = 0; c0 < nchunk; c0 += kCPL * MOE_WAVE) {
+    float acc[kCPL][8];
 #pragma unroll
-      for (int u = 0; u < kKU; ++u) {
-        const int k = k0 + u;
-        const int s = k < K ? so[k] : -1;
-        ok[u] = s >= 0 && s < rows_cap;
-        const uint4* row = reinterpret_cast<const uint4*>(eo + static_cast<int64_t>(ok[u] ? s : 0) * H * IB +
-                                                          static_cast<int64_t>(c) * 8 * IB);
+    for (int u = 0; u < kCPL; ++u)
 #pragma unroll
-        for (int v = 0; v < (IB == 2 ? 1 : 2); ++v)
-          raw[u][v] = ok[u] ? row[v] : make_uint4(0, 0, 0, 0);
+      for (int i = 0; i < 8; ++i) acc[u][i] = 0.f;
+    for (uint64_t m = routes; m; m &= m - 1) {
+      const int k = __builtin_ctzll(m);            // increasing k
+      const int s = __builtin_amdgcn_readlane(s_l, k);
+      const float wk = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w_l), k));
+      const uint4* row = reinterpret_cast<const uint4*>(eo + static_cast<int64_t>(s) * H * IB);
+      uint4 raw[kCPL][NV];
+#pragma unroll
+      for (int u = 0; u < kCPL; ++u) {
+        const int c = c0 + u * MOE_WAVE + lane;
+#pragma unroll
+        for (int v = 0; v < NV; ++v)
+          raw[u][v] = c < nchunk ? row[static_cast<int64_t>(c) * NV + v] : make_uint4(0, 0, 0, 0);
       }
 #pragma unroll
-      for (int u = 0; u < kKU; ++u) {
-        if (!ok[u]) continue;
-        const float wk = wt[k0 + u];
+      for (int u = 0; u < kCPL; ++u) {
         float v[8];
         if constexpr (kInBf16) {
           const uint32_t ww[4] = {raw[u][0].x, raw[u][0].y, raw[u][0].z, raw[u][0].w};
@@ -124,7 +132,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const uint8_t* __rest
           }
         } else {
           const uint32_t ww[8] = {raw[u][0].x, raw[u][0].y, raw[u][0].z, raw[u][0].w,
-                                  raw[u][1].x, raw[u][1].y, raw[u][1].z, raw[u][1].w};
+                                  raw[u][NV - 1].x, raw[u][NV - 1].y, raw[u][NV - 1].z, raw[u][NV - 1].w};
 #pragma unroll
           for (int i = 0; i < 8; ++i) v[i] = __uint_as_float(ww[i]);
         }
@@ -132,21 +140,26 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const uint8_t* __rest
           // product and sum rounded separately, in k order (no FMA contraction)
 #pragma clang fp contract(off)
 #pragma unroll
-          for (int i = 0; i < 8; ++i) acc[i] = acc[i] + wk * v[i];
+          for (int i = 0; i < 8; ++i) acc[u][i] = acc[u][i] + wk * v[i];
         }
       }
     }
-    uint8_t* dst = y + static_cast<int64_t>(t) * H * OB + static_cast<int64_t>(c) * 8 * OB;
-    if constexpr (kOutBf16) {
-      uint4 o;
-      o.x = moe::f32_to_bf16(acc[0]) | (uint32_t(moe::f32_to_bf16(acc[1])) << 16);
-      o.y = moe::f32_to_bf16(acc[2]) | (uint32_t(moe::f32_to_bf16(acc[3])) << 16);
-      o.z = moe::f32_to_bf16(acc[4]) | (uint32_t(moe::f32_to_bf16(acc[5])) << 16);
-      o.w = moe::f32_to_bf16(acc[6]) | (uint32_t(moe::f32_to_bf16(acc[7])) << 16);
-      moe::store_nt16(dst, o);
-    } else {
-      reinterpret_cast<float4*>(dst)[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
-      reinterpret_cast<float4*>(dst)[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+#pragma unroll
+    for (int u = 0; u < kCPL; ++u) {
+      const int c = c0 + u * MOE_WAVE + lane;
+      if (c >= nchunk) break;
+      uint8_t* dst = yrow + static_cast<int64_t>(c) * 8 * OB;
+      if constexpr (kOutBf16) {
+        uint4 o;
+        o.x = moe::f32_to_bf16(acc[u][0]) | (uint32_t(moe::f32_to_bf16(acc[u][1])) << 16);
+        o.y = moe::f32_to_bf16(acc[u][2]) | (uint32_t(moe::f32_to_bf16(acc[u][3])) << 16);
+        o.z = moe::f32_to_bf16(acc[u][4]) | (uint32_t(moe::f32_to_bf16(acc[u][5])) << 16);
+        o.w = moe::f32_to_bf16(acc[u][6]) | (uint32_t(moe::f32_to_bf16(acc[u][7])) << 16);
+        moe::store_nt16(dst, o);
+      } else {
+        reinterpret_cast<float4*>(dst)[0] = make_float4(acc[u][0], acc[u][1], acc[u][2], acc[u][3]);
+        reinterpret_cast<float4*>(dst)[1] = make_float4(acc[u][4], acc[u][5], acc[u][6], acc[u][7]);
+      }
     }
   }
 }

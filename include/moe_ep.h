@@ -126,7 +126,7 @@ moe_status moe_dispatch_layout(const int32_t* topk_ids, int T, int K, int E_glob
  *   slot_of    [T,K]  from moe_dispatch_layout (values >= rows_cap are skipped)
  *   buf        [rows_cap,H]  buf_dt: same as x_dt, or MOE_FP8_E4M3
  *   buf_scales [rows_cap,H/128] fp32 when buf_dt == MOE_FP8_E4M3, else unused
- * Limits: H % 128 == 0.  Padding rows of buf are left untouched.
+ * Limits: H % 128 == 0, K <= 64.  Padding rows of buf are left untouched.
  */
 moe_status moe_permute(const void* x, moe_dtype x_dt, int T, int K, int H,
                        const int32_t* slot_of, int64_t rows_cap,
@@ -205,7 +205,7 @@ moe_status moe_grouped_gemm_w2(const void* z, moe_dtype z_dt, const float* z_sca
  * combine_convert).
  *   expert_out [rows_cap,H] eo_dt in {F32, BF16};  slot_of [T,K];
  *   topk_weights [T,K] fp32;  y [T,H] y_dt in {F32, BF16}
- * Limits: H % 8 == 0.
+ * Limits: H % 8 == 0, K <= 64.
  */
 moe_status moe_combine(const void* expert_out, moe_dtype eo_dt, const int32_t* slot_of,
                        const float* topk_weights, int T, int K, int H, int64_t rows_cap,

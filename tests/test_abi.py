@@ -104,6 +104,7 @@ def test_permute_argument_errors(lib):
     assert f(P(), 2, 4, 2, 256, P(), 8, P(), 2, P(), None) == UNSUPPORTED   # fp8 input
     assert f(P(), 1, 4, 2, 256, P(), 8, P(), 2, None, None) == INVALID      # fp8 without scales
     assert f(P(), 7, 4, 2, 256, P(), 8, P(), 1, None, None) == INVALID      # bad dtype enum
+    assert f(P(), 1, 4, 65, 256, P(), 8, P(), 1, None, None) == UNSUPPORTED  # K > 64 routes
     assert f(None, 1, 0, 2, 256, None, 8, None, 1, None, None) == OK        # T = 0: nothing to do
 
 
@@ -143,6 +144,7 @@ def test_combine_and_silu_argument_errors(lib):
                   ctypes.c_void_p]
     assert c(P(), 1, P(), P(), 4, 2, 100, 8, P(), 1, None) == UNSUPPORTED    # H % 8
     assert c(P(), 2, P(), P(), 4, 2, 256, 8, P(), 1, None) == UNSUPPORTED    # fp8 outputs
+    assert c(P(), 1, P(), P(), 4, 65, 256, 8, P(), 1, None) == UNSUPPORTED   # K > 64 routes
     assert c(P(), 1, None, P(), 4, 2, 256, 8, P(), 1, None) == INVALID
     s = lib.moe_silu_mul
     s.restype = ctypes.c_int
