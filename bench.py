@@ -34,7 +34,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="prefill_fp8")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=6144)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=8192)
     ap.add_argument("--skip-cpu-baseline", action="store_true",
                     help="omit the oracle timing (profiling runs)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
