@@ -7,9 +7,10 @@ It shares no code, tables or helpers with the HIP path.
 
 Plain, slow, obviously correct: numpy, fp64 dot products, Python loops where
 the pages describe a sequential procedure.  Each function cites the page
-passage it follows; see ``formats`` (number formats) and ``moe`` (the path).
+passage it follows; see ``formats`` (number formats), ``moe`` (the path) and
+``router`` (the router top-k step in front of it).
 
 Every function here is pinned by ``tests/test_oracle_*.py`` against facts the
 pages print, closed forms, invariants, library routines or brute force.
 """
-from . import formats, moe  # noqa: F401
+from . import formats, moe, router  # noqa: F401
