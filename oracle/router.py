@@ -47,7 +47,7 @@ def router_topk(logits: np.ndarray, K: int, bias: np.ndarray | None = None,
 
         def rank_key(e):
             v = float(row[e])
-            return (math.inf if math.isnan(v) else -v, e)
+            return (1, 0.0, e) if math.isnan(v) else (0, -v, e)   # NaN after every number
 
         order = sorted(range(E), key=rank_key)[:K]
         v = [float(base[t, e]) for e in order]

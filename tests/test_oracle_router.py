@@ -81,3 +81,7 @@ def test_nan_ranks_last():
     x = np.array([[np.nan, -1e30, 0.5]], np.float32)
     ids, w = router.router_topk(x, 2)
     assert list(ids[0]) == [2, 1]
+    # below -inf too, whatever its id
+    x = np.array([[np.nan, -np.inf, np.inf, -0.0, 0.0]], np.float32)
+    ids, _ = router.router_topk(x, 5)
+    assert list(ids[0]) == [2, 3, 4, 1, 0]                             # -0 and +0 tie: lower id first
