@@ -119,6 +119,36 @@ def cpu_baseline(wl, n_tokens):
                       f"weight dequantisation, fp64 GEMMs, combine); {dt:.1f} s"}
 
 
+def router_timing(cfg, steps, dev):
+    """moe_router_topk on the workload's router inputs, timed on its own (it
+    produces the routing the step starts from, so it is not part of a step).
+    Bytes: logits read + bias read + ids and weights written."""
+    import torch
+
+    import combine_top_expert_amd as ep
+    from workloads import make_router_inputs
+
+    logits, bias = make_router_inputs(cfg)
+    lg = torch.from_numpy(logits).to(dev)
+    b = None if bias is None else torch.from_numpy(bias).to(dev)
+    ids = torch.empty((cfg.T, cfg.K), dtype=torch.int32, device=dev)
+    w = torch.empty((cfg.T, cfg.K), dtype=torch.float32, device=dev)
+    for _ in range(3):
+        ep.moe_router_topk(lg, cfg.K, ids, w, bias=b)
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n = max(steps, 10)
+    e0.record(stream)
+    for _ in range(n):
+        ep.moe_router_topk(lg, cfg.K, ids, w, bias=b)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / n
+    nbytes = cfg.T * cfg.E * 4 + cfg.E * 4 + cfg.T * cfg.K * 8
+    return {"us": us, "bytes": nbytes, "gbs": nbytes / (us * 1e-6) / 1e9,
+            "shape": {"T": cfg.T, "E": cfg.E, "K": cfg.K, "bias": cfg.bias}}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -253,6 +283,8 @@ def main():
     out["stage_gbs"] = {"permute": perm_bytes / (stage_us["permute"] * 1e-6) / 1e9,
                         "combine": comb_bytes / (stage_us["combine"] * 1e-6) / 1e9}
 
+    if cfg.routing == "softmax":
+        out["next_rows"] = {"router_topk": router_timing(cfg, args.steps, dev)}
     if not args.skip_cpu_baseline:
         print("[bench] cpu baseline (oracle sample)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_sample_tokens)

@@ -5,7 +5,7 @@ dtype and contiguity, derives sizes from shapes, and calls the C entry point
 of the same name in ``include/moe_ep.h`` on torch's current HIP stream.
 All computation happens in the library's HIP kernels; there is no CPU or
 PyTorch fallback.  Importing this package fails loudly if the library has
-not been built (``python -m combine_top_expert_amd.build``).
+not been built (``python combine_top_expert_amd/build.py``).
 """
 from __future__ import annotations
 
@@ -20,7 +20,7 @@ __all__ = [
     "MOE_EPI_STORE_G", "MOE_EPI_SILU_MUL", "MOE_FLAG_CAPACITY", "MOE_FLAG_BAD_EXPERT_ID",
     "moe_status_string", "moe_abi_version", "moe_dispatch_layout_workspace_bytes",
     "moe_dispatch_layout", "moe_permute", "moe_grouped_gemm_w13", "moe_silu_mul",
-    "moe_grouped_gemm_w2", "moe_combine", "dtype_code",
+    "moe_grouped_gemm_w2", "moe_combine", "moe_router_topk", "dtype_code",
 ]
 
 LIB_PATH = Path(os.environ.get("MOE_EP_LIB", Path(__file__).resolve().parent / "libmoe_ep.so"))
@@ -30,7 +30,7 @@ MOE_EPI_STORE_G, MOE_EPI_SILU_MUL = 0, 1
 MOE_FLAG_CAPACITY, MOE_FLAG_BAD_EXPERT_ID = 1, 2
 
 if not LIB_PATH.exists():
-    raise ImportError(f"{LIB_PATH} is not built; run `python -m combine_top_expert_amd.build` "
+    raise ImportError(f"{LIB_PATH} is not built; run `python combine_top_expert_amd/build.py` "
                       "(the MoE path has no fallback without its HIP library)")
 lib = ctypes.CDLL(str(LIB_PATH))
 
@@ -45,8 +45,12 @@ _SIG = {
     "moe_silu_mul": (_i, [_p, _p, _p, _i, _i64, _i, _p, _i, _p, _p]),
     "moe_grouped_gemm_w2": (_i, [_p, _i, _p, _p, _i, _p, _p, _p, _i, _i64, _i, _i, _p, _i, _p]),
     "moe_combine": (_i, [_p, _i, _p, _p, _i, _i, _i, _i64, _p, _i, _p]),
+    "moe_router_topk": (_i, [_p, _p, _i, _i, _i, _i, _p, _p, _p]),
 }
 for _name, (_res, _args) in _SIG.items():
+    if not hasattr(lib, _name):
+        raise ImportError(f"{LIB_PATH} lacks {_name}: it predates these sources; rebuild with "
+                          "`python combine_top_expert_amd/build.py`")
     _f = getattr(lib, _name)
     _f.restype, _f.argtypes = _res, _args
 
@@ -172,3 +176,11 @@ def moe_combine(expert_out, slot_of, topk_weights, y) -> None:
         _ptr(expert_out, "expert_out"), dtype_code(expert_out), _i32(slot_of, "slot_of"),
         _f32(topk_weights, "topk_weights"), T, K, H, expert_out.shape[0], _ptr(y, "y"),
         dtype_code(y), _stream(y)))
+
+
+def moe_router_topk(logits, K, topk_ids, topk_weights, bias=None, bias_in_weights=True) -> None:
+    """logits [T,E] fp32 (+ bias [E] fp32) -> topk_ids [T,K] int32, topk_weights [T,K] fp32."""
+    T, E = logits.shape
+    _check("moe_router_topk", lib.moe_router_topk(
+        _f32(logits, "logits"), _f32(bias, "bias"), T, E, K, 1 if bias_in_weights else 0,
+        _i32(topk_ids, "topk_ids"), _f32(topk_weights, "topk_weights"), _stream(logits)))

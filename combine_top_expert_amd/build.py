@@ -1,6 +1,9 @@
 """Build libmoe_ep.so (gfx950) in-tree with hipcc.
 
-    python -m combine_top_expert_amd.build [--jobs N]
+    python combine_top_expert_amd/build.py [--jobs N]
+
+(Run it as a script, not as ``-m combine_top_expert_amd.build``: importing the
+package loads the library, which may be missing or stale before a build.)
 
 Compiles every source under csrc/ to an object in _build/ (in parallel) and
 links them into combine_top_expert_amd/libmoe_ep.so.  Always rebuilds.

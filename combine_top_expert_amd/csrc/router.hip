@@ -1,0 +1,129 @@
+// moe_router_topk: router logits -> top-K expert ids and renormalised
+// softmax weights, the TopKOutput the dispatch path starts from ("SGLang、
+// NCCL 与 MoE EP" §1.1: router scores, a selection policy returns K ids and
+// weights; §3.6: topk_ids [T,K], topk_weights [T,K]).
+//
+// One wavefront per token.  Lane l holds the scores of experts l, l+64, ...
+// (score = logit + bias, one fp32 add).  Each of the K rounds takes the
+// wave-wide maximum of a 64-bit key -- an order-preserving integer image of
+// the score in the high word (NaN lowest, -0 folded onto +0) and the
+// complement of the expert id in the low word, so equal scores go to the
+// lower id -- and retires the winner.  Lane k keeps round k's expert; the K
+// lanes then form exp(v - max) and its sum with wave reductions, and divide.
+
+#include "moe_common.h"
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kTokPerBlock = kThreads / MOE_WAVE;
+constexpr int kMaxE = 1024;
+constexpr int kMaxK = 64;
+
+// order-preserving image of an fp32 value: larger float -> larger key;
+// every NaN maps below -inf, -0 and +0 map together
+__device__ __forceinline__ uint32_t score_key(float v) {
+  if (v != v) return 0u;
+  uint32_t u = __float_as_uint(v == 0.0f ? 0.0f : v);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t k) {
+#pragma unroll
+  for (int d = 1; d < MOE_WAVE; d <<= 1) {
+    const uint32_t lo = __shfl_xor(static_cast<uint32_t>(k), d);
+    const uint32_t hi = __shfl_xor(static_cast<uint32_t>(k >> 32), d);
+    const uint64_t o = (static_cast<uint64_t>(hi) << 32) | lo;
+    k = o > k ? o : k;
+  }
+  return k;
+}
+
+__device__ __forceinline__ float wave_max_f32(float v) {
+#pragma unroll
+  for (int d = 1; d < MOE_WAVE; d <<= 1) v = fmaxf(v, __shfl_xor(v, d));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum_f32(float v) {
+#pragma unroll
+  for (int d = 1; d < MOE_WAVE; d <<= 1) v += __shfl_xor(v, d);
+  return v;
+}
+
+template <int NPL>   // scores per lane: E <= 64 * NPL
+__global__ __launch_bounds__(kThreads) void router_topk_kernel(const float* __restrict__ logits,
+                                                               const float* __restrict__ bias, int T,
+                                                               int E, int K, int bias_in_weights,
+                                                               int32_t* __restrict__ ids,
+                                                               float* __restrict__ weights) {
+  const int lane = moe::lane_id();
+  const int t = blockIdx.x * kTokPerBlock + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const float* row = logits + static_cast<int64_t>(t) * E;
+  uint64_t key[NPL];
+#pragma unroll
+  for (int j = 0; j < NPL; ++j) {
+    const int e = lane + MOE_WAVE * j;
+    key[j] = 0;                                  // absent: below every real entry
+    if (e < E) {
+      const float v = bias ? row[e] + bias[e] : row[e];
+      // low word 0xffffffff - e > 0, so a present entry (even a NaN score,
+      // high word 0) always beats an absent or retired one (key 0)
+      key[j] = (static_cast<uint64_t>(score_key(v)) << 32) | (0xffffffffu - static_cast<uint32_t>(e));
+    }
+  }
+  int my_id = -1;
+  float my_v = 0.0f;
+  for (int k = 0; k < K; ++k) {
+    uint64_t best = 0;
+    int bj = -1;
+#pragma unroll
+    for (int j = 0; j < NPL; ++j)
+      if (key[j] > best) { best = key[j]; bj = j; }
+    const uint64_t win = wave_max_u64(best);
+    const int e = static_cast<int>(0xffffffffu - static_cast<uint32_t>(win));
+    if (bj >= 0 && best == win) {               // the owning lane retires the winner
+#pragma unroll
+      for (int j = 0; j < NPL; ++j)
+        if (j == bj) key[j] = 0;
+    }
+    if (lane == k) my_id = e;
+  }
+  // the value entering the weights: the score, or the unbiased logit when
+  // the bias only steers the selection
+  if (lane < K) my_v = (bias && bias_in_weights) ? row[my_id] + bias[my_id] : row[my_id];
+  const float m = wave_max_f32(lane < K ? my_v : -INFINITY);
+  const float p = lane < K ? expf(my_v - m) : 0.0f;
+  const float s = wave_sum_f32(p);
+  if (lane < K) {
+    ids[static_cast<int64_t>(t) * K + lane] = my_id;
+    weights[static_cast<int64_t>(t) * K + lane] = p / s;
+  }
+}
+
+template <int NPL>
+void launch(const float* logits, const float* bias, int T, int E, int K, int biw, int32_t* ids,
+            float* w, hipStream_t stream) {
+  const int grid = (T + kTokPerBlock - 1) / kTokPerBlock;
+  router_topk_kernel<NPL><<<grid, kThreads, 0, stream>>>(logits, bias, T, E, K, biw, ids, w);
+}
+
+}  // namespace
+
+extern "C" moe_status moe_router_topk(const float* logits, const float* bias, int T, int E, int K,
+                                      int bias_in_weights, int32_t* topk_ids, float* topk_weights,
+                                      hipStream_t stream) {
+  MOE_CHECK(T >= 0 && E >= 1 && K >= 1 && K <= E, MOE_ERR_INVALID_ARG);
+  MOE_CHECK(E <= kMaxE && K <= kMaxK, MOE_ERR_UNSUPPORTED);
+  if (T == 0) return MOE_OK;
+  MOE_CHECK(logits && topk_ids && topk_weights, MOE_ERR_INVALID_ARG);
+  const int biw = bias_in_weights ? 1 : 0;
+  if (E <= 64) launch<1>(logits, bias, T, E, K, biw, topk_ids, topk_weights, stream);
+  else if (E <= 128) launch<2>(logits, bias, T, E, K, biw, topk_ids, topk_weights, stream);
+  else if (E <= 256) launch<4>(logits, bias, T, E, K, biw, topk_ids, topk_weights, stream);
+  else if (E <= 512) launch<8>(logits, bias, T, E, K, biw, topk_ids, topk_weights, stream);
+  else launch<16>(logits, bias, T, E, K, biw, topk_ids, topk_weights, stream);
+  MOE_LAUNCH_CHECK();
+  return MOE_OK;
+}

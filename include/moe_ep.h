@@ -70,7 +70,7 @@ typedef enum moe_w13_epilogue {
 /* Human-readable name of a moe_status value (static string). */
 const char* moe_status_string(int status);
 
-/* ABI version; bumped on any signature change. */
+/* ABI version; bumped on any signature change or added entry point (2: moe_router_topk). */
 int moe_abi_version(void);
 
 /* Bytes of device workspace moe_dispatch_layout needs for (T, K, L). */
@@ -210,6 +210,30 @@ moe_status moe_grouped_gemm_w2(const void* z, moe_dtype z_dt, const float* z_sca
 moe_status moe_combine(const void* expert_out, moe_dtype eo_dt, const int32_t* slot_of,
                        const float* topk_weights, int T, int K, int H, int64_t rows_cap,
                        void* y, moe_dtype y_dt, hipStream_t stream);
+
+/*
+ * moe_router_topk -- router logits -> the TopKOutput the path starts from.
+ *
+ * The router scores every expert and a selection policy returns K expert
+ * ids and K weights per token ([EP] §1.1; §3.6 TopKOutput topk_ids [T,K],
+ * topk_weights [T,K]).  The pages leave the arithmetic to the model; this
+ * entry point implements the renormalised-softmax top-K:
+ *   score[t,e]  = logits[t,e] + bias[e]  (one fp32 add; bias may be NULL)
+ *   topk_ids[t,k]  = expert with the k-th largest score, k = 0 largest;
+ *                    equal scores go to the lower expert id; a NaN score
+ *                    ranks below every number
+ *   topk_weights[t,k] = exp(v_k - max v) / sum_j exp(v_j - max v) over the
+ *                    K selected experts (fp32), v = score, or the unbiased
+ *                    logit when bias_in_weights == 0 (bias steers the
+ *                    selection only); NaN if a selected value is NaN
+ *   logits [T,E] fp32 row-major (device); bias [E] fp32 (device) or NULL;
+ *   topk_ids [T,K] int32 and topk_weights [T,K] fp32 (device, written).
+ * Limits: 1 <= K <= E, E <= 1024, K <= 64.  Returns MOE_ERR_INVALID_ARG
+ * for K > E or missing pointers, MOE_ERR_UNSUPPORTED beyond the limits.
+ */
+moe_status moe_router_topk(const float* logits, const float* bias, int T, int E, int K,
+                           int bias_in_weights, int32_t* topk_ids, float* topk_weights,
+                           hipStream_t stream);
 
 #ifdef __cplusplus
 }

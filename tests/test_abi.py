@@ -26,17 +26,17 @@ def declared_functions():
 @pytest.fixture(scope="module")
 def lib():
     if not LIB.exists():
-        from combine_top_expert_amd.build import build
-        build(verbose=False)
+        import __graft_entry__
+        __graft_entry__._build_module().build(verbose=False)
     return ctypes.CDLL(str(LIB))
 
 
-def test_header_declares_the_six_entry_points():
+def test_header_declares_the_entry_points():
     fns = declared_functions()
     for name in ["moe_dispatch_layout", "moe_permute", "moe_grouped_gemm_w13", "moe_silu_mul",
-                 "moe_grouped_gemm_w2", "moe_combine"]:
+                 "moe_grouped_gemm_w2", "moe_combine", "moe_router_topk"]:
         assert name in fns
-    assert len(fns) == 9
+    assert len(fns) == 10
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -54,7 +54,7 @@ def test_status_strings_and_version(lib):
     assert lib.moe_status_string(0) == b"MOE_OK"
     assert lib.moe_status_string(-2) == b"MOE_ERR_UNSUPPORTED"
     assert lib.moe_status_string(12345) == b"MOE_ERR_UNKNOWN"
-    assert lib.moe_abi_version() == 1
+    assert lib.moe_abi_version() == 2
 
 
 def test_workspace_bytes(lib):
@@ -158,7 +158,7 @@ def test_python_binding_loads_and_matches_header(lib):
     import combine_top_expert_amd as ep
     for name in declared_functions():
         assert callable(getattr(ep, name)), name
-    assert ep.moe_abi_version() == 1
+    assert ep.moe_abi_version() == 2
     assert ep.moe_status_string(-1) == "MOE_ERR_INVALID_ARG"
 
 
@@ -176,3 +176,16 @@ def test_product_never_touches_the_oracle():
         text = f.read_text()
         assert not re.search(r"^\s*(from|import)\s+(oracle|workloads)\b", text, flags=re.M), f
         assert "oracle/" not in text, f
+
+
+def test_router_argument_errors(lib):
+    r = lib.moe_router_topk
+    r.restype = ctypes.c_int
+    r.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                  ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    assert r(P(), None, 4, 8, 9, 1, P(), P(), None) == INVALID          # K > E
+    assert r(P(), None, 4, 8, 0, 1, P(), P(), None) == INVALID          # K = 0
+    assert r(P(), None, 4, 2048, 8, 1, P(), P(), None) == UNSUPPORTED   # E > 1024
+    assert r(P(), None, 4, 256, 65, 1, P(), P(), None) == UNSUPPORTED   # K > 64
+    assert r(None, None, 4, 256, 8, 1, P(), P(), None) == INVALID       # no logits
+    assert r(None, None, 0, 256, 8, 1, None, None, None) == OK          # T = 0

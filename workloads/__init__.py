@@ -178,6 +178,21 @@ def make_routing(cfg: MoEConfig):
     raise ValueError(f"routing {cfg.routing!r} has no generated ids")
 
 
+def make_router_inputs(cfg: MoEConfig, seed_stream: int = 7):
+    """Router logits [T,E] fp32 ~ N(0,1) and the per-expert fp32 bias of the
+    workload's routing recipe (None without one): the inputs of the router
+    top-k step, drawn from their own seeded stream."""
+    logits = _rng(cfg.seed, seed_stream).standard_normal((cfg.T, cfg.E), dtype=np.float32)
+    e = np.arange(cfg.E, dtype=np.float64)
+    if cfg.bias == "linear":
+        bias = cfg.bias_alpha * (e % cfg.L) / max(cfg.L - 1, 1)
+    elif cfg.bias == "zipf":
+        bias = -cfg.bias_alpha * np.log(e + 1.0)
+    else:
+        return logits, None
+    return logits, bias.astype(np.float32)
+
+
 # ----------------------------------------------------------------------------
 # activations and weights
 
