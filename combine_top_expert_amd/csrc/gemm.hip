@@ -146,15 +146,6 @@ __device__ __forceinline__ uint32_t lds_u32(const void* p) {
                :                                                                           \
                : "memory")
 
-// Keeps the fp32 folds of a read phase before its closing barrier.
-#define MOE_PIN_ACC(acc)                                                                    \
-  asm volatile(""                                                                          \
-               : "+v"(acc[0][0][0]), "+v"(acc[0][0][1]), "+v"(acc[0][1][0]), "+v"(acc[0][1][1]), \
-                 "+v"(acc[1][0][0]), "+v"(acc[1][0][1]), "+v"(acc[1][1][0]), "+v"(acc[1][1][1]), \
-                 "+v"(acc[2][0][0]), "+v"(acc[2][0][1]), "+v"(acc[2][1][0]), "+v"(acc[2][1][1]), \
-                 "+v"(acc[3][0][0]), "+v"(acc[3][0][1]), "+v"(acc[3][1][0]), "+v"(acc[3][1][1])  \
-               :)
-
 // Workgroup barriers that also pin register values: the compiler may move
 // matrix instructions (they touch no memory) across a plain barrier, which
 // would blur the phases; routing the fragments (resp. accumulators) through

@@ -101,6 +101,6 @@ inline bool valid_dtype(int d) { return d == MOE_F32 || d == MOE_BF16 || d == MO
 inline int elem_bytes(moe_dtype d) { return d == MOE_F32 ? 4 : (d == MOE_BF16 ? 2 : 1); }
 
 // Compute units of the current device (cached per device id).
-int device_cu_count();
+__attribute__((visibility("hidden"))) int device_cu_count();
 
 }  // namespace moe_host
