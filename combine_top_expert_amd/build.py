@@ -62,7 +62,10 @@ def build(jobs: int = 8, verbose: bool = True) -> Path:
     with ThreadPoolExecutor(max_workers=max(1, min(jobs, len(srcs)))) as ex:
         objs = list(ex.map(_compile, srcs))
     tmp = LIB.with_suffix(".so.tmp")
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", str(tmp), *map(str, objs)]
+    # --no-undefined: an unresolved symbol (e.g. a kernel stub the host pass
+    # did not emit) fails the build instead of the first dlopen
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Wl,--no-undefined", "-o", str(tmp),
+           *map(str, objs)]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

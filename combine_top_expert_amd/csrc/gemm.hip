@@ -206,6 +206,15 @@ __device__ __forceinline__ void decode_tile(int L, int nb_count, int t, int& e, 
   mt = local - nb * mte;
 }
 
+// Staging context of one tile, workgroup-uniform.
+struct Tile {
+  int e, nb, rows_valid, n0;
+  int64_t row0;
+  bool half1;
+  int a_row_off, w_row_off, s_row_off;
+  int ws0, ws1;                        // FP8: first weight-scale index of each half
+};
+
 template <int DT, int EPI>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs p) {
   const int tid = threadIdx.x;
@@ -278,68 +287,105 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs p) {
   const int fc1 = ((2 * (lane >> 4) + 1) ^ fsw) << 4;
   const uint32_t ring = lds_u32(s_ring);
 
-  for (int t = t_begin; t < t_end; t += t_step) {
+  // Per-tile staging context (see Tile).  The tile decode reads LDS, so
+  // readfirstlane marks its results workgroup-uniform.
+  auto make_tile = [&](int t) {
+    Tile c;
     int e, nb, mt;
     decode_tile(p.L, p.nb_count, t, e, nb, mt);
-    const int rows_valid = min(BM, eff_count(p, e) - mt * BM);
-    const int64_t row0 = static_cast<int64_t>(p.offsets[e]) + static_cast<int64_t>(mt) * BM;
-    const int n0 = nb * p.nb_stride;
-    const bool half1 = n0 + p.half_stride < p.N;
-
-    // Buffer resources: A over the whole expert-major buffer, W over this
-    // expert's [N, K] block.  Rows past the end of a resource read as 0, so
-    // a tail tile may read past its expert's last row without a clamp; those
-    // rows are never stored.
-    const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint8_t*>(p.A), 0, static_cast<int>(p.rows_cap * lda), kRsrcWord3);
+    c.e = __builtin_amdgcn_readfirstlane(e);
+    c.nb = __builtin_amdgcn_readfirstlane(nb);
+    mt = __builtin_amdgcn_readfirstlane(mt);
+    c.rows_valid = min(BM, eff_count(p, c.e) - mt * BM);
+    c.row0 = static_cast<int64_t>(p.offsets[c.e]) + static_cast<int64_t>(mt) * BM;
+    c.n0 = c.nb * p.nb_stride;
+    c.half1 = c.n0 + p.half_stride < p.N;
+    // this wave stages A rows 16*wave + [0,16) and W-tile rows 32*wave +
+    // [0,32) (waves 0-3: half 0, waves 4-7: half 1)
+    c.a_row_off = static_cast<int>((c.row0 + 16 * wave) * lda);
+    c.w_row_off = static_cast<int>((c.n0 + (wave >> 2) * (c.half1 ? p.half_stride : 0) + 32 * (wave & 3)) * lda);
+    c.s_row_off = static_cast<int>((c.row0 + 16 * wave) * kgroups * 4);
+    const int bpe = p.N / 128;                 // weight-scale block rows per expert
+    c.ws0 = (c.e * bpe + c.n0 / 128) * kgroups;
+    c.ws1 = (c.e * bpe + (c.half1 ? c.n0 + p.half_stride : c.n0) / 128) * kgroups;
+    return c;
+  };
+  // Buffer resources: A over the whole expert-major buffer, W over one
+  // expert's [N, K] block.  Rows past the end of a resource read as 0, so a
+  // tail tile may read past its expert's last row without a clamp; those
+  // rows are never stored.
+  const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(p.A), 0, static_cast<int>(p.rows_cap * lda), kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rS = kFp8 ? __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(p.As), 0, static_cast<int>(p.rows_cap * kgroups * 4), kRsrcWord3) : rA;
+  // issue this wave's direct-to-LDS loads of K stage ks of tile c into slot s
+  auto issue = [&](const Tile& c, int s, int ks) {
     const __amdgpu_buffer_rsrc_t rW = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint8_t*>(p.W + static_cast<int64_t>(e) * p.N * lda), 0,
+        const_cast<uint8_t*>(p.W + static_cast<int64_t>(c.e) * p.N * lda), 0,
         static_cast<int>(p.N * lda), kRsrcWord3);
-    // this wave stages A rows 16*wave + [0,16) and W-tile rows 32*wave + [0,32)
-    // (waves 0-3: half 0, waves 4-7: half 1)
-    const int a_row_off = static_cast<int>((row0 + 16 * wave) * lda);
-    const int w_row = n0 + (wave >> 2) * (half1 ? p.half_stride : 0) + 32 * (wave & 3);
-    const int w_row_off = static_cast<int>(w_row * lda);
-    __amdgpu_buffer_rsrc_t rS = rA;              // FP8: the A-scale buffer
-    int s_row_off = 0;
-    float vsw[2][2] = {{0.f, 0.f}, {0.f, 0.f}};   // weight scales of the tile, lane g = group g
+    uint8_t* st = s_ring + s * STAGE;
+    typedef __attribute__((address_space(3))) void* lds_void;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rA, (lds_void)(st + (16 * wave + 8 * j) * KB), 16, j ? voff_o : voff_e,
+          c.a_row_off + static_cast<int>(8 * j * lda) + ks * KB, 0, 0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rW, (lds_void)(st + A_BYTES + (32 * wave + 8 * j) * KB), 16, (j & 1) ? voff_o : voff_e,
+          c.w_row_off + static_cast<int>(8 * j * lda) + ks * KB, 0, 0);
     if constexpr (kFp8) {
-      rS = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(p.As), 0,
-                                             static_cast<int>(p.rows_cap * kgroups * 4), kRsrcWord3);
-      s_row_off = static_cast<int>((row0 + 16 * wave) * kgroups * 4);
-      const float* wse = p.Ws + static_cast<int64_t>(e) * (p.N / 128) * kgroups;
-      const float* w0 = wse + static_cast<int64_t>(n0 / 128) * kgroups;
-      const float* w1 = wse + static_cast<int64_t>((half1 ? n0 + p.half_stride : n0) / 128) * kgroups;
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const int g = lane + 64 * q;
-        vsw[0][q] = g < kgroups ? w0[g] : 0.f;
-        vsw[1][q] = g < kgroups ? w1[g] : 0.f;
-      }
-      // these loads must not be in flight once the staged loads start
-      __builtin_amdgcn_s_waitcnt(VmCnt<0>::imm);
+      if (lane < 16)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rS, (lds_void)(st + A_BYTES + B_BYTES + 16 * wave * 4), 4, soff, c.s_row_off + ks * 4, 0, 0);
     }
+  };
 
-    // issue the direct-to-LDS loads of K stage ks into ring slot s
-    auto issue = [&](int s, int ks) {
-      uint8_t* st = s_ring + s * STAGE;
-      typedef __attribute__((address_space(3))) void* lds_void;
+  // The workgroup's tiles form one stream of stages: stage g is K stage
+  // g % kstages of its (g / kstages)-th tile and lives in ring slot g % NST.
+  // With kstages >= 2, the first two stages of the next tile are staged
+  // during the last two stages of the current one, so a tile starts with its
+  // operands on the way instead of refilling the pipeline.
+  const int my_tiles = t_begin < t_end ? (t_end - t_begin + t_step - 1) / t_step : 0;
+  const int total = my_tiles * kstages;
+  const bool stream = kstages >= 2;
+  // FP8 weight scales of a tile: lane g holds group g (and 64 + g) of each
+  // half; read per stage with readlane
+  auto load_wscales = [&](const Tile& c, float (&v)[2][2]) {
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rA, (lds_void)(st + (16 * wave + 8 * j) * KB), 16, j ? voff_o : voff_e,
-            a_row_off + static_cast<int>(8 * j * lda) + ks * KB, 0, 0);
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rW, (lds_void)(st + A_BYTES + (32 * wave + 8 * j) * KB), 16, (j & 1) ? voff_o : voff_e,
-            w_row_off + static_cast<int>(8 * j * lda) + ks * KB, 0, 0);
-      if constexpr (kFp8) {
-        if (lane < 16)
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(
-              rS, (lds_void)(st + A_BYTES + B_BYTES + 16 * wave * 4), 4, soff, s_row_off + ks * 4, 0, 0);
-      }
+    for (int q = 0; q < 2; ++q) {
+      const int g = lane + 64 * q;
+      v[0][q] = g < kgroups ? p.Ws[c.ws0 + g] : 0.f;
+      v[1][q] = g < kgroups ? p.Ws[c.ws1 + g] : 0.f;
+    }
+  };
+  Tile cur{}, nxt{};
+  float vsw[2][2] = {{0.f, 0.f}, {0.f, 0.f}}, vsw_n[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
+  if (my_tiles > 0) {
+    cur = make_tile(t_begin);
+    if constexpr (kFp8) load_wscales(cur, vsw);
+  }
+  if (my_tiles > 1) {
+    nxt = make_tile(t_begin + t_step);
+    if constexpr (kFp8) load_wscales(nxt, vsw_n);
+  }
+  const uint32_t a_frag = (wm * 64 + frow) * KB;
+  const uint32_t b_frag = A_BYTES + (wn * 32 + frow) * KB;
+  const uint32_t s_frag = A_BYTES + B_BYTES + (wm * 64 + (lane >> 4) * 4) * 4;
+
+  for (int ti = 0; ti < my_tiles; ++ti) {
+    const int base = ti * kstages;             // stream index of this tile's stage 0
+    const int e = cur.e, nb = cur.nb, rows_valid = cur.rows_valid, n0 = cur.n0;
+    const int64_t row0 = cur.row0;
+    const bool half1 = cur.half1;
+    // stage g of the stream exists / is staged by the code below
+    auto staged = [&](int g) { return g < total && (stream || g < base + kstages); };
+    auto issue_g = [&](int g) {
+      const int ks = g - base;
+      if (ks < kstages) issue(cur, g % NST, ks); else issue(nxt, g % NST, ks - kstages);
     };
+    (void)e;
 
     v4f acc[4][2][2];
 #pragma unroll
@@ -349,37 +395,38 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs p) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][h][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    __syncthreads();               // every wave is done with the ring of the previous tile
-    issue(0, 0);
-    if (kstages > 1) {
-      issue(1, 1);
-      __builtin_amdgcn_s_waitcnt(VmCnt<NLOAD>::imm);
-    } else {
+    if (ti == 0 || !stream) {
+      // nothing of a previous tile is still landing in the ring
       __builtin_amdgcn_s_waitcnt(VmCnt<0>::imm);
+      __syncthreads();
+      issue_g(base);
+      if (staged(base + 1)) {
+        issue_g(base + 1);
+        __builtin_amdgcn_s_waitcnt(VmCnt<NLOAD>::imm);
+      } else {
+        __builtin_amdgcn_s_waitcnt(VmCnt<0>::imm);
+      }
+      __builtin_amdgcn_s_barrier();  // stage 0 has landed for every wave
     }
-    __builtin_amdgcn_s_barrier();  // stage 0 has landed for every wave
 
     // Two wave groups take turns.  Every phase ends with a workgroup
     // barrier; in each phase one group stages and reads while the other runs
     // the matrix products of the stage it read in the phase before, so each
     // SIMD always has one wave feeding the matrix core and one moving data.
-    // Group g reads stage ks in global phase 2*ks + g and multiplies it in
-    // phase 2*ks + g + 1 (group 1 waits out phase 0, group 0 the last phase).
-    // In its read phase for stage ks a wave also issues its share of stage
-    // ks + 2 (into the slot of stage ks - 1, which group 1 finished reading
-    // in phase 2*ks - 1) and, before the closing barrier, waits for its own
-    // loads of stage ks + 1 -- so neither staging issue nor waits ever sit in
-    // a matrix phase.  Stage ks + 1 is first read in phase 2*ks + 2, after
-    // both groups' waits.
-    const uint32_t a_frag = (wm * 64 + frow) * KB;
-    const uint32_t b_frag = A_BYTES + (wn * 32 + frow) * KB;
-    const uint32_t s_frag = A_BYTES + B_BYTES + (wm * 64 + (lane >> 4) * 4) * 4;
+    // Group g reads stage ks in phase 2*ks + g and multiplies it in phase
+    // 2*ks + g + 1 (group 1 waits out phase 0, group 0 the last phase).  In
+    // its read phase for stream stage G a wave also issues its share of
+    // stage G + 2 (into the slot of G - 1, which group 1 finished reading in
+    // the phase before) and, before the closing barrier, waits for its own
+    // loads of stage G + 1 -- so neither staging issue nor waits ever sit in
+    // a matrix phase.  Stage G + 1 is first read after both groups' waits.
     if (wm == 1) __builtin_amdgcn_s_barrier();
     for (int ks = 0; ks < kstages; ++ks) {
+      const int g = base + ks;
       // fragment reads first (no wait), then the staging loads: a wave is
       // held at a staging load until the memory pipeline takes it, and the
       // reads complete meanwhile
-      const uint32_t sb = ring + (ks % NST) * STAGE;
+      const uint32_t sb = ring + (g % NST) * STAGE;
       u4 af[8], bf[8], sv[4];
       MOE_DS_AB(af, bf, sb + a_frag + fc0, sb + a_frag + fc1, sb + b_frag + fc0, sb + b_frag + fc1);
       if constexpr (kFp8) {
@@ -387,10 +434,10 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs p) {
       } else {
         sv[0] = sv[1] = sv[2] = sv[3] = u4{0, 0, 0, 0};
       }
-      if (ks + 2 < kstages) issue((ks + 2) % NST, ks + 2);
-      if (ks + 2 < kstages)
+      if (staged(g + 2)) issue_g(g + 2);
+      if (staged(g + 2))
         __builtin_amdgcn_s_waitcnt(VmCnt<NLOAD>::imm);
-      else if (ks + 1 < kstages)
+      else if (staged(g + 1))
         __builtin_amdgcn_s_waitcnt(VmCnt<0>::imm);
       MOE_WAIT_BARRIER_FRAGS(af, bf, sv);
       if constexpr (kFp8) {
@@ -521,6 +568,18 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs p) {
             }
           }
       }
+    }
+    // the next tile's first stages are already on their way
+    cur = nxt;
+    if constexpr (kFp8) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int q = 0; q < 2; ++q) vsw[h][q] = vsw_n[h][q];
+    }
+    if (ti + 2 < my_tiles) {
+      nxt = make_tile(t_begin + (ti + 2) * t_step);
+      if constexpr (kFp8) load_wscales(nxt, vsw_n);
     }
   }
 }

@@ -2,11 +2,13 @@
 
 The kernel keeps three LDS stages in a ring and splits its 8 waves into two
 groups that alternate read and matrix phases, one phase apart; every phase
-ends with a workgroup barrier.  In its read phase for stage ks a wave issues
-its direct-to-LDS loads of stage ks + 2 and, before the closing barrier,
-waits (vmcnt) until its own loads of stage ks + 1 have landed.  This test
-replays that program order for both groups and every stage count up to 129
-and checks the two properties the kernel relies on:
+ends with a workgroup barrier.  A workgroup's tiles form one stream of
+stages; in its read phase for stream stage G a wave issues its
+direct-to-LDS loads of stage G + 2 (possibly the next tile's) and, before the
+closing barrier, waits (vmcnt) until its own loads of stage G + 1 have
+landed.  This test replays that program order for both groups, for 1, 2 and
+5 tiles of many stage counts, and checks the two properties the kernel
+relies on:
 
 * every read of stage s by either group comes after a barrier that follows
   every wave's wait for stage s;
@@ -18,35 +20,52 @@ import pytest
 NST = 3          # LDS ring depth
 
 
-def wave_program(group, K):
-    ev = [("issue", 0)]
-    if K > 1:
-        ev += [("issue", 1), ("wait", 1)]      # stage 0 landed, stage 1 may be in flight
-    else:
-        ev += [("wait", 0)]
-    ev.append(("bar", None))
-    if group == 1:
-        ev.append(("bar", None))               # group 1 sits out phase 0
-    for ks in range(K):
-        if ks + 2 < K:
-            ev.append(("issue", ks + 2))
-        ev.append(("read", ks))
-        if ks + 2 < K:
-            ev.append(("wait", 1))
-        elif ks + 1 < K:
-            ev.append(("wait", 0))
-        ev.append(("bar", None))               # end of read phase
-        ev.append(("bar", None))               # end of matrix phase
-    if group == 0:
-        ev.append(("bar", None))               # group 0 sits out the last phase
+def wave_program(group, K, tiles=1):
+    """Program order of one wave over `tiles` tiles of K stages each.  The
+    stages of all tiles form one stream (stage g = K stage g % K of tile
+    g // K, slot g % NST); with K >= 2 the next tile's first stages are
+    staged during the current tile, otherwise each tile refills the ring."""
+    total = tiles * K
+    stream = K >= 2
+    ev = []
+    for ti in range(tiles):
+        base = ti * K
+
+        def staged(g):
+            return g < total and (stream or g < base + K)
+
+        if ti == 0 or not stream:
+            ev += [("wait", 0), ("bar", None)]         # ring idle
+            ev.append(("issue", base))
+            if staged(base + 1):
+                ev += [("issue", base + 1), ("wait", 1)]
+            else:
+                ev.append(("wait", 0))
+            ev.append(("bar", None))
+        if group == 1:
+            ev.append(("bar", None))                  # group 1 sits out the tile's phase 0
+        for ks in range(K):
+            g = base + ks
+            if staged(g + 2):
+                ev.append(("issue", g + 2))
+            ev.append(("read", g))
+            if staged(g + 2):
+                ev.append(("wait", 1))
+            elif staged(g + 1):
+                ev.append(("wait", 0))
+            ev.append(("bar", None))                  # end of read phase
+            ev.append(("bar", None))                  # end of matrix phase
+        if group == 0:
+            ev.append(("bar", None))                  # group 0 sits out the last phase
+        ev.append(("bar", None))                      # epilogue barrier (FP8 Z amax)
     return ev
 
 
-def replay(K):
+def replay(K, tiles=1):
     info = {}
     for g in (0, 1):
         b, issued, landed_at, reads, issues = 0, [], {}, [], []
-        for kind, a in wave_program(g, K):
+        for kind, a in wave_program(g, K, tiles):
             if kind == "bar":
                 b += 1
             elif kind == "issue":
@@ -61,9 +80,10 @@ def replay(K):
     return info
 
 
-@pytest.mark.parametrize("K", list(range(1, 130)))
-def test_staging_protocol(K):
-    info = replay(K)
+@pytest.mark.parametrize("tiles", [1, 2, 5])
+@pytest.mark.parametrize("K", list(range(1, 40)) + [56, 64, 112, 128])
+def test_staging_protocol(K, tiles):
+    info = replay(K, tiles)
     assert info[0][0] == info[1][0], "both groups must pass the same number of barriers"
     for g in (0, 1):
         for s, b in info[g][2]:
@@ -83,12 +103,12 @@ def test_protocol_model_detects_a_missing_wait():
     global wave_program
     orig = wave_program
 
-    def broken(group, K):
-        return [e for e in orig(group, K) if not (group == 1 and e == ("wait", 1))]
+    def broken(group, K, tiles=1):
+        return [e for e in orig(group, K, tiles) if not (group == 1 and e == ("wait", 1))]
 
     try:
         wave_program = broken
         with pytest.raises(AssertionError):
-            test_staging_protocol(8)
+            test_staging_protocol(8, 2)
     finally:
         wave_program = orig
