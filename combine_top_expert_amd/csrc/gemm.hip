@@ -21,30 +21,40 @@
 // halves are the gate block n0 + [0,128) and the matching up block
 // I + n0 + [0,128), so one lane holds gate and up of the same (row, column)
 // and SiLU(gate)*up needs no data exchange.  For W2 the halves are two
-// adjacent 128-column blocks.  Eight waves (two per SIMD, so one wave's LDS
-// reads overlap the other's matrix work) in a 2x4 grid each own 64 rows x
-// (32 columns of each half) = 16 MFMA 16x16 tiles.
+// adjacent 128-column blocks.
+//
+// Waves.  Twelve waves, three per SIMD.  Waves 8-11 are producers: they
+// only move K stages HBM -> LDS with direct-to-LDS buffer loads (lane l's
+// bytes land at base + size*l), so a wave held at a load issue by the
+// memory pipeline never holds up matrix work.  Waves 0-7 are consumers in
+// a 2 x 4 grid, each owning 64 rows x (32 columns of each half) = 16 MFMA
+// 16x16 tiles; they only read LDS and multiply.
 //
 // K loop.  One stage = 128 bytes of K per row: 128 FP8, 64 bf16 or 32 fp32
 // values -- for FP8 exactly one activation / weight scale group.  Each
 // lane's MFMA operand is 32 contiguous bytes of one row of the stage, so
 // the same LDS fragment feeds one 16x16x128 FP8 MFMA, two 16x16x32 bf16
-// MFMAs or eight 16x16x4 fp32 MFMAs (A and B use the same K mapping, so the
-// dot products pair up).
+// MFMAs or eight 16x16x4 fp32 MFMAs (both operands use the same K mapping,
+// so the dot products pair up).  The weight fragment is the matrix unit's
+// first operand and the activation fragment its second, so a lane's four
+// results of a 16x16 tile are four consecutive output columns of ONE
+// activation row: a lane needs one activation scale per 16-row block.
 //
-// Stages move HBM -> LDS by direct-to-LDS loads (global_load_lds_dwordx4:
-// lane l's 16 bytes land at base + 16*l), three stages deep, so two stages
-// are in flight while the third is multiplied and no VGPR holds staged data.
-// A stage row is 128 bytes in a 16-byte XOR swizzle (chunk c of row r at
-// chunk c ^ ((r >> 1) & 7), bank-conflict free on the 64-bank LDS); the
-// swizzle is applied by choosing which source chunk each lane fetches.  Fragment reads are issued as ds_read_b128 in inline
-// assembly that ends with its own lgkmcnt wait, so the compiler never
-// inserts a full vmcnt wait (which would drain the loads still in flight);
-// stage completion is tracked by hand with vmcnt and a workgroup barrier.
+// Ring and phases.  Three stages live in an LDS ring.  Consumer waves 0-3
+// and 4-7 form two groups that alternate a read phase (fragment reads of a
+// stage) and a matrix phase (its products), one phase apart, so each SIMD
+// has one consumer on the matrix core while the other reads; a workgroup
+// barrier, taken by all twelve waves, closes every phase.  In the two
+// phases of stream stage G the producers issue stage G + 2 (into the slot
+// of G - 1, whose last reader finished in the phase before) and then wait
+// (vmcnt) for their loads of G + 1, which the consumers first read after
+// the second barrier.
 //
 // FP8 scaling.  Per stage g every 16x16 FP8 product P_g is formed from a
 // zero accumulator and folded in as acc += P_g * (a_scale[row, g] *
-// w_scale[block, g]), fp32.
+// w_scale[block, g]), fp32.  Both scales travel with the stage: the
+// activation scales of the 128 rows and the two weight-block scales are
+// staged into LDS beside the operands.
 
 #include <algorithm>
 
@@ -53,11 +63,14 @@
 namespace {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int i4 __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float f2 __attribute__((ext_vector_type(2)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
-typedef uint32_t u4 __attribute__((ext_vector_type(4)));   // 16 bytes in 4 VGPRs
 
-constexpr int kThreads = 512;
+constexpr int kConsumers = 8;      // consumer waves, 2 x 4 grid
+constexpr int kProducers = 4;      // staging waves
+constexpr int kThreads = (kConsumers + kProducers) * MOE_WAVE;
 constexpr int BM = 128;            // rows per tile
 constexpr int BH = 128;            // columns per half
 constexpr int KB = 128;            // bytes of K per stage and row
@@ -65,9 +78,11 @@ constexpr int kMaxL = 1024;
 constexpr int NST = 3;             // LDS ring depth
 constexpr int A_BYTES = BM * KB;                   // 16 KB
 constexpr int B_BYTES = 2 * BH * KB;               // 32 KB
-constexpr int AS_BYTES = BM * 4;                   // FP8 activation scales
-constexpr int STAGE = A_BYTES + B_BYTES + AS_BYTES;
+constexpr int AS_BYTES = BM * 4;                   // FP8 activation scales of the stage
+constexpr int WS_BYTES = 16;                       // FP8 weight scales of the two halves (+ pad)
+constexpr int STAGE = A_BYTES + B_BYTES + AS_BYTES + WS_BYTES;
 constexpr int kRsrcWord3 = 0x00020000;             // raw buffer: 32-bit data format
+static_assert(STAGE % 16 == 0, "stage slots must stay 16-byte aligned");
 
 enum Dt { DT_F32 = 0, DT_BF16 = 1, DT_FP8 = 2 };
 enum Epi { EPI_STORE_F32 = 0, EPI_STORE_BF16 = 1, EPI_SILU_F32 = 2, EPI_SILU_BF16 = 3, EPI_SILU_FP8 = 4 };
@@ -93,10 +108,17 @@ struct GemmArgs {
 
 // Rows of expert e that exist: counts[e] clipped to the buffer, so a tile
 // never reaches past rows_cap even for inconsistent counts/offsets.
-__device__ __forceinline__ int eff_count(const GemmArgs& p, int e) {
-  const int64_t off = p.offsets[e];
-  if (off < 0 || off >= p.rows_cap) return 0;
-  return static_cast<int>(max<int64_t>(0, min<int64_t>(p.counts[e], p.rows_cap - off)));
+__device__ __forceinline__ int eff_count(int64_t off, int cnt, int64_t rows_cap) {
+  if (off < 0 || off >= rows_cap) return 0;
+  return static_cast<int>(max<int64_t>(0, min<int64_t>(cnt, rows_cap - off)));
+}
+
+// counts / offsets of a workgroup-uniform expert through the scalar cache:
+// scalar loads complete on lgkmcnt, so they never add to the vmcnt queue
+// that tracks the staged loads
+typedef const __attribute__((address_space(4))) int32_t* cint_ptr;
+__device__ __forceinline__ int32_t uniform_load(const int32_t* base, int i) {
+  return ((cint_ptr)base)[i];
 }
 
 // s_waitcnt immediate for "vmcnt <= n" with the other counters left alone
@@ -104,83 +126,52 @@ template <int N> struct VmCnt {
   static constexpr int imm = (N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8);
 };
 
-// byte address of a __shared__ object inside the workgroup's LDS
-__device__ __forceinline__ uint32_t lds_u32(const void* p) {
-  typedef const __attribute__((address_space(3))) uint8_t* lds_ptr;
-  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr)(p)));
-}
+// Workgroup barrier that is also a compiler fence: no memory access moves
+// across it.
+__device__ __forceinline__ void wg_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
-// Fragment reads of one stage for one wave, issued without waiting: A (4
-// row sub-tiles) and B (half, 16-column sub-tile) at (0,0) (0,1) (1,0)
-// (1,1); for FP8 the activation scales of the wave's 64 rows.  The
-// registers are only consumed after MOE_WAIT_BARRIER_FRAGS, which waits for
-// them (lgkmcnt) and carries them as operands.
-#define MOE_DS_AB(af, bf, a0, a1, b0, b1)                                                    \
-  asm volatile(                                                                            \
-      "ds_read_b128 %0, %16\n ds_read_b128 %1, %17\n"                                      \
-      "ds_read_b128 %2, %16 offset:2048\n ds_read_b128 %3, %17 offset:2048\n"              \
-      "ds_read_b128 %4, %16 offset:4096\n ds_read_b128 %5, %17 offset:4096\n"              \
-      "ds_read_b128 %6, %16 offset:6144\n ds_read_b128 %7, %17 offset:6144\n"              \
-      "ds_read_b128 %8, %18\n ds_read_b128 %9, %19\n"                                      \
-      "ds_read_b128 %10, %18 offset:2048\n ds_read_b128 %11, %19 offset:2048\n"            \
-      "ds_read_b128 %12, %18 offset:16384\n ds_read_b128 %13, %19 offset:16384\n"          \
-      "ds_read_b128 %14, %18 offset:18432\n ds_read_b128 %15, %19 offset:18432"             \
-      : "=&v"(af[0]), "=&v"(af[1]), "=&v"(af[2]), "=&v"(af[3]), "=&v"(af[4]), "=&v"(af[5]), \
-        "=&v"(af[6]), "=&v"(af[7]), "=&v"(bf[0]), "=&v"(bf[1]), "=&v"(bf[2]), "=&v"(bf[3]), \
-        "=&v"(bf[4]), "=&v"(bf[5]), "=&v"(bf[6]), "=&v"(bf[7])                              \
-      : "v"(a0), "v"(a1), "v"(b0), "v"(b1))
-
-#define MOE_DS_S(sv, s0)                                                                    \
-  asm volatile(                                                                            \
-      "ds_read_b128 %0, %4\n ds_read_b128 %1, %4 offset:64\n"                              \
-      "ds_read_b128 %2, %4 offset:128\n ds_read_b128 %3, %4 offset:192"                    \
-      : "=&v"(sv[0]), "=&v"(sv[1]), "=&v"(sv[2]), "=&v"(sv[3])                              \
-      : "v"(s0))
-
-#define MOE_WAIT_BARRIER_FRAGS(af, bf, sv)                                                  \
-  asm volatile("s_waitcnt lgkmcnt(0)\n s_barrier"                                          \
-               : "+v"(af[0]), "+v"(af[1]), "+v"(af[2]), "+v"(af[3]), "+v"(af[4]), "+v"(af[5]), \
-                 "+v"(af[6]), "+v"(af[7]), "+v"(bf[0]), "+v"(bf[1]), "+v"(bf[2]), "+v"(bf[3]), \
-                 "+v"(bf[4]), "+v"(bf[5]), "+v"(bf[6]), "+v"(bf[7]), "+v"(sv[0]), "+v"(sv[1]), \
-                 "+v"(sv[2]), "+v"(sv[3])                                                   \
-               :                                                                           \
+// End of a consumer's read phase: its fragment reads of the stage are
+// complete (the slot may be re-staged after the barrier) and the fragments
+// pass through the barrier as register operands, so no product that uses
+// them can be scheduled before it.
+#define MOE_WAIT_BARRIER_FRAGS(af, bf, sa, sw)                                                \
+  asm volatile("s_waitcnt lgkmcnt(0)\n s_barrier"                                            \
+               : "+v"(af[0]), "+v"(af[1]), "+v"(af[2]), "+v"(af[3]), "+v"(bf[0][0]),          \
+                 "+v"(bf[0][1]), "+v"(bf[1][0]), "+v"(bf[1][1]), "+v"(sa), "+v"(sw)            \
+               :                                                                             \
                : "memory")
 
-// Workgroup barriers that also pin register values: the compiler may move
-// matrix instructions (they touch no memory) across a plain barrier, which
-// would blur the phases; routing the fragments (resp. accumulators) through
-// the barrier keeps the products of a phase between its two barriers.
-#define MOE_BARRIER_ACC(acc, WAIT)                                                          \
-  asm volatile(WAIT "s_barrier"                                                            \
+// End of a matrix phase: the accumulators pass through the barrier, so the
+// products of the phase stay between its two barriers.
+#define MOE_BARRIER_ACC(acc)                                                                  \
+  asm volatile("s_barrier"                                                                   \
                : "+v"(acc[0][0][0]), "+v"(acc[0][0][1]), "+v"(acc[0][1][0]), "+v"(acc[0][1][1]), \
                  "+v"(acc[1][0][0]), "+v"(acc[1][0][1]), "+v"(acc[1][1][0]), "+v"(acc[1][1][1]), \
                  "+v"(acc[2][0][0]), "+v"(acc[2][0][1]), "+v"(acc[2][1][0]), "+v"(acc[2][1][1]), \
                  "+v"(acc[3][0][0]), "+v"(acc[3][0][1]), "+v"(acc[3][1][0]), "+v"(acc[3][1][1])  \
-               :                                                                           \
+               :                                                                             \
                : "memory")
 
+// One 16x16 product over one stage: w = 16 weight rows (first operand),
+// a = 16 activation rows (second operand); lane l holds 32 bytes of row
+// l & 15 at K bytes 32 * (l >> 4).  Result: lane l, element r = output
+// column 4 * (l >> 4) + r of activation row l & 15.
 template <int DT>
-__device__ __forceinline__ v4f mma_stage(const u4& alo, const u4& ahi, const u4& blo,
-                                         const u4& bhi, v4f acc) {
+__device__ __forceinline__ v4f mma_stage(const v8i& w, const v8i& a, v4f acc) {
   if constexpr (DT == DT_FP8) {
-    const v8i a = {int(alo.x), int(alo.y), int(alo.z), int(alo.w), int(ahi.x), int(ahi.y), int(ahi.z), int(ahi.w)};
-    const v8i b = {int(blo.x), int(blo.y), int(blo.z), int(blo.w), int(bhi.x), int(bhi.y), int(bhi.z), int(bhi.w)};
-    // formats 0/0 = fp8 e4m3 for A and B; scale bytes 127 = 2^0
-    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc, 0, 0, 0, 127, 0, 127);
+    // formats 0/0 = fp8 e4m3 for both operands; scale bytes 127 = 2^0
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(w, a, acc, 0, 0, 0, 127, 0, 127);
   } else if constexpr (DT == DT_BF16) {
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, alo),
-                                                 __builtin_bit_cast(v8bf, blo), acc, 0, 0, 0);
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, ahi),
-                                                  __builtin_bit_cast(v8bf, bhi), acc, 0, 0, 0);
+    const i4 wl = __builtin_shufflevector(w, w, 0, 1, 2, 3), wh = __builtin_shufflevector(w, w, 4, 5, 6, 7);
+    const i4 al = __builtin_shufflevector(a, a, 0, 1, 2, 3), ah = __builtin_shufflevector(a, a, 4, 5, 6, 7);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, wl), __builtin_bit_cast(v8bf, al),
+                                                 acc, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, wh), __builtin_bit_cast(v8bf, ah),
+                                                  acc, 0, 0, 0);
   } else {
-    const float a[8] = {__uint_as_float(alo.x), __uint_as_float(alo.y), __uint_as_float(alo.z),
-                        __uint_as_float(alo.w), __uint_as_float(ahi.x), __uint_as_float(ahi.y),
-                        __uint_as_float(ahi.z), __uint_as_float(ahi.w)};
-    const float b[8] = {__uint_as_float(blo.x), __uint_as_float(blo.y), __uint_as_float(blo.z),
-                        __uint_as_float(blo.w), __uint_as_float(bhi.x), __uint_as_float(bhi.y),
-                        __uint_as_float(bhi.z), __uint_as_float(bhi.w)};
 #pragma unroll
-    for (int m = 0; m < 8; ++m) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[m], b[m], acc, 0, 0, 0);
+    for (int m = 0; m < 8; ++m)
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__int_as_float(w[m]), __int_as_float(a[m]), acc, 0, 0, 0);
     return acc;
   }
 }
@@ -206,14 +197,20 @@ __device__ __forceinline__ void decode_tile(int L, int nb_count, int t, int& e, 
   mt = local - nb * mte;
 }
 
-// Staging context of one tile, workgroup-uniform.
+// One tile, workgroup-uniform.
 struct Tile {
   int e, nb, rows_valid, n0;
   int64_t row0;
   bool half1;
-  int a_row_off, w_row_off, s_row_off;
   int ws0, ws1;                        // FP8: first weight-scale index of each half
 };
+
+// 32 bytes of one LDS row for an MFMA operand: 16-byte chunks at c0 and c1
+__device__ __forceinline__ v8i lds_frag(const uint8_t* row, int c0, int c1) {
+  const i4 lo = *reinterpret_cast<const i4*>(row + c0);
+  const i4 hi = *reinterpret_cast<const i4*>(row + c1);
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
 
 template <int DT, int EPI>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs p) {
@@ -222,18 +219,19 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs p) {
   // wave-uniform by construction; readfirstlane tells the compiler so, which
   // keeps the staged-load offsets in scalar registers (no per-load loop)
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 2;      // 64-row slice of the tile = wave group (0: waves 0-3, 1: 4-7)
-  const int wn = wave & 3;       // 32-column slice of each half
   constexpr int ESZ = DT == DT_FP8 ? 1 : (DT == DT_BF16 ? 2 : 4);
   constexpr bool kFp8 = DT == DT_FP8;
-  constexpr int NLOAD = kFp8 ? 7 : 6;      // direct-to-LDS loads per wave per stage
+  // direct-to-LDS loads per producer per stage (producer 0 issues one more,
+  // the weight scales, first)
+  constexpr int NLOAD = kFp8 ? 13 : 12;
 
   // ---- tile map: row tiles per expert, prefix over experts (block scan)
   {
     const int per = (p.L + kThreads - 1) / kThreads;
     const int e0 = tid * per;
     int s = 0;
-    for (int e = e0; e < min(e0 + per, p.L); ++e) s += (eff_count(p, e) + BM - 1) / BM;
+    for (int e = e0; e < min(e0 + per, p.L); ++e)
+      s += (eff_count(p.offsets[e], p.counts[e], p.rows_cap) + BM - 1) / BM;
     s_part[tid] = s;
     __syncthreads();
     for (int d = 1; d < kThreads; d <<= 1) {
@@ -245,7 +243,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs p) {
     int run = s_part[tid] - s;     // exclusive prefix of this thread's range
     for (int e = e0; e < min(e0 + per, p.L); ++e) {
       s_mt_prefix[e] = run;
-      run += (eff_count(p, e) + BM - 1) / BM;
+      run += (eff_count(p.offsets[e], p.counts[e], p.rows_cap) + BM - 1) / BM;
     }
     if (tid == kThreads - 1) s_mt_prefix[p.L] = s_part[kThreads - 1];
     __syncthreads();
@@ -268,27 +266,6 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs p) {
   const int kgroups = p.K / 128;              // FP8 scale groups along K
   const int64_t lda = static_cast<int64_t>(p.K) * ESZ;
 
-  // Stage layout: chunk c (16 bytes) of row r sits at chunk c ^ swz(r) with
-  // swz(r) = (r & 7) ^ ((r >> 3) & 1), which repeats every 16 rows.  With it
-  // the fragment reads below (16 rows x 4 chunk pairs per instruction) run
-  // at the full LDS rate with no bank conflicts (measured: 256 B/clk per CU
-  // with 8 waves; the same reads without the (r >> 3) term, or with
-  // (r >> 1) & 7, reach 160 B/clk).  A direct-to-LDS load still writes 1 KB
-  // contiguously: lane l fills row srow = l >> 3 of an 8-row group g,
-  // physical chunk l & 7, so it fetches chunk (l & 7) ^ srow ^ (g & 1).
-  const int srow = lane >> 3;
-  const int voff_e = static_cast<int>(srow * lda) + (((lane & 7) ^ srow) << 4);
-  const int voff_o = static_cast<int>(srow * lda) + (((lane & 7) ^ srow ^ 1) << 4);
-  const int soff = (lane & 15) * kgroups * 4;    // A-scale row of this lane (FP8)
-  // fragment reads: row (lane & 15) of a 16-row block, bytes 32*(lane>>4)..+32
-  const int frow = lane & 15;
-  const int fsw = (frow & 7) ^ (frow >> 3);
-  const int fc0 = ((2 * (lane >> 4)) ^ fsw) << 4;
-  const int fc1 = ((2 * (lane >> 4) + 1) ^ fsw) << 4;
-  const uint32_t ring = lds_u32(s_ring);
-
-  // Per-tile staging context (see Tile).  The tile decode reads LDS, so
-  // readfirstlane marks its results workgroup-uniform.
   auto make_tile = [&](int t) {
     Tile c;
     int e, nb, mt;
@@ -296,50 +273,15 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs p) {
     c.e = __builtin_amdgcn_readfirstlane(e);
     c.nb = __builtin_amdgcn_readfirstlane(nb);
     mt = __builtin_amdgcn_readfirstlane(mt);
-    c.rows_valid = min(BM, eff_count(p, c.e) - mt * BM);
-    c.row0 = static_cast<int64_t>(p.offsets[c.e]) + static_cast<int64_t>(mt) * BM;
+    const int64_t off = uniform_load(p.offsets, c.e);
+    c.rows_valid = min(BM, eff_count(off, uniform_load(p.counts, c.e), p.rows_cap) - mt * BM);
+    c.row0 = off + static_cast<int64_t>(mt) * BM;
     c.n0 = c.nb * p.nb_stride;
     c.half1 = c.n0 + p.half_stride < p.N;
-    // this wave stages A rows 16*wave + [0,16) and W-tile rows 32*wave +
-    // [0,32) (waves 0-3: half 0, waves 4-7: half 1)
-    c.a_row_off = static_cast<int>((c.row0 + 16 * wave) * lda);
-    c.w_row_off = static_cast<int>((c.n0 + (wave >> 2) * (c.half1 ? p.half_stride : 0) + 32 * (wave & 3)) * lda);
-    c.s_row_off = static_cast<int>((c.row0 + 16 * wave) * kgroups * 4);
     const int bpe = p.N / 128;                 // weight-scale block rows per expert
     c.ws0 = (c.e * bpe + c.n0 / 128) * kgroups;
     c.ws1 = (c.e * bpe + (c.half1 ? c.n0 + p.half_stride : c.n0) / 128) * kgroups;
     return c;
-  };
-  // Buffer resources: A over the whole expert-major buffer, W over one
-  // expert's [N, K] block.  Rows past the end of a resource read as 0, so a
-  // tail tile may read past its expert's last row without a clamp; those
-  // rows are never stored.
-  const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t*>(p.A), 0, static_cast<int>(p.rows_cap * lda), kRsrcWord3);
-  const __amdgpu_buffer_rsrc_t rS = kFp8 ? __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<float*>(p.As), 0, static_cast<int>(p.rows_cap * kgroups * 4), kRsrcWord3) : rA;
-  // issue this wave's direct-to-LDS loads of K stage ks of tile c into slot s
-  auto issue = [&](const Tile& c, int s, int ks) {
-    const __amdgpu_buffer_rsrc_t rW = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint8_t*>(p.W + static_cast<int64_t>(c.e) * p.N * lda), 0,
-        static_cast<int>(p.N * lda), kRsrcWord3);
-    uint8_t* st = s_ring + s * STAGE;
-    typedef __attribute__((address_space(3))) void* lds_void;
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rA, (lds_void)(st + (16 * wave + 8 * j) * KB), 16, j ? voff_o : voff_e,
-          c.a_row_off + static_cast<int>(8 * j * lda) + ks * KB, 0, 0);
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rW, (lds_void)(st + A_BYTES + (32 * wave + 8 * j) * KB), 16, (j & 1) ? voff_o : voff_e,
-          c.w_row_off + static_cast<int>(8 * j * lda) + ks * KB, 0, 0);
-    if constexpr (kFp8) {
-      if (lane < 16)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rS, (lds_void)(st + A_BYTES + B_BYTES + 16 * wave * 4), 4, soff, c.s_row_off + ks * 4, 0, 0);
-    }
   };
 
   // The workgroup's tiles form one stream of stages: stage g is K stage
@@ -350,42 +292,137 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs p) {
   const int my_tiles = t_begin < t_end ? (t_end - t_begin + t_step - 1) / t_step : 0;
   const int total = my_tiles * kstages;
   const bool stream = kstages >= 2;
-  // FP8 weight scales of a tile: lane g holds group g (and 64 + g) of each
-  // half; read per stage with readlane
-  auto load_wscales = [&](const Tile& c, float (&v)[2][2]) {
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int g = lane + 64 * q;
-      v[0][q] = g < kgroups ? p.Ws[c.ws0 + g] : 0.f;
-      v[1][q] = g < kgroups ? p.Ws[c.ws1 + g] : 0.f;
-    }
-  };
   Tile cur{}, nxt{};
-  float vsw[2][2] = {{0.f, 0.f}, {0.f, 0.f}}, vsw_n[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
-  if (my_tiles > 0) {
-    cur = make_tile(t_begin);
-    if constexpr (kFp8) load_wscales(cur, vsw);
+  if (my_tiles > 0) cur = make_tile(t_begin);
+  if (my_tiles > 1) nxt = make_tile(t_begin + t_step);
+
+  if (wave >= kConsumers) {
+    // ================================================================ producers
+    // Stage layout: chunk c (16 bytes) of row r sits at chunk c ^ swz(r) with
+    // swz(r) = (r & 7) ^ ((r >> 3) & 1), which repeats every 16 rows; with it
+    // the consumers' fragment reads (16 rows x 2 chunks per lane group) hit
+    // every LDS bank once.  A direct-to-LDS load still writes 1 KB
+    // contiguously: lane l fills row l >> 3 of an 8-row group, physical chunk
+    // l & 7, so it fetches chunk (l & 7) ^ (l >> 3) ^ (group & 1).
+    //   producer w stages A rows 32w + [0,32), W rows 64w + [0,64) (w < 2:
+    //   half 0, else half 1), FP8 activation-scale positions 32w + [0,32),
+    //   and producer 0 the two weight scales.  Scale position 64m + 4q + i
+    //   holds row 64m + 16i + q, so a consumer lane of row group m reads the
+    //   four scales of its rows 16i + q with one 16-byte read.
+    const int pw = wave - kConsumers;
+    const int srow = lane >> 3;
+    const int voff_e = static_cast<int>(srow * lda) + (((lane & 7) ^ srow) << 4);
+    const int voff_o = static_cast<int>(srow * lda) + (((lane & 7) ^ srow ^ 1) << 4);
+    const int spos = 32 * (pw & 1) + (lane & 31);
+    const int soff = (64 * (pw >> 1) + 16 * (spos & 3) + (spos >> 2)) * kgroups * 4;
+    // Buffer resources: A over the whole expert-major buffer, W over one
+    // expert's [N, K] block.  Rows past the end of a resource read as 0, so a
+    // tail tile may read past its expert's last row without a clamp; those
+    // rows are never stored.
+    const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(p.A), 0, static_cast<int>(p.rows_cap * lda), kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rS = kFp8 ? __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(p.As), 0, static_cast<int>(p.rows_cap * kgroups * 4), kRsrcWord3) : rA;
+    const __amdgpu_buffer_rsrc_t rWs = kFp8 ? __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(p.Ws), 0, p.L * (p.N / 128) * kgroups * 4, kRsrcWord3) : rA;
+    typedef __attribute__((address_space(3))) void* lds_void;
+
+    // half 0 / half 1 of this producer's loads of K stage ks of tile c into
+    // ring slot s (FP8: 7 + 6 loads, plus the weight scales on producer 0)
+    auto issue_half = [&](const Tile& c, int s, int ks, int half) {
+      const __amdgpu_buffer_rsrc_t rW = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint8_t*>(p.W + static_cast<int64_t>(c.e) * p.N * lda), 0,
+          static_cast<int>(p.N * lda), kRsrcWord3);
+      uint8_t* st = s_ring + s * STAGE;
+      if constexpr (kFp8) {
+        if (half == 0 && pw == 0 && lane < 2)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rWs, (lds_void)(st + A_BYTES + B_BYTES + AS_BYTES), 4,
+                                                   (lane ? c.ws1 : c.ws0) * 4, ks * 4, 0, 0);
+      }
+      const int a_off = static_cast<int>((c.row0 + 32 * pw) * lda) + ks * KB;
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        const int j = 2 * half + jj;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_void)(st + (32 * pw + 8 * j) * KB), 16,
+                                                 (j & 1) ? voff_o : voff_e,
+                                                 a_off + static_cast<int>(8 * j * lda), 0, 0);
+      }
+      const int w_off =
+          static_cast<int>((c.n0 + (pw >> 1) * (c.half1 ? p.half_stride : 0) + 64 * (pw & 1)) * lda) + ks * KB;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int j = 4 * half + jj;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rW, (lds_void)(st + A_BYTES + (64 * pw + 8 * j) * KB), 16,
+                                                 (j & 1) ? voff_o : voff_e,
+                                                 w_off + static_cast<int>(8 * j * lda), 0, 0);
+      }
+      if constexpr (kFp8) {
+        if (half == 0 && lane < 32)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rS, (lds_void)(st + A_BYTES + B_BYTES + 128 * pw), 4, soff,
+                                                   static_cast<int>(c.row0 * kgroups * 4) + ks * 4, 0, 0);
+      }
+    };
+
+    for (int ti = 0; ti < my_tiles; ++ti) {
+      const int base = ti * kstages;           // stream index of this tile's stage 0
+      auto staged = [&](int g) { return g < total && (stream || g < base + kstages); };
+      auto issue_g = [&](int g, int half) {
+        const int ks = g - base;
+        if (ks < kstages) issue_half(cur, g % NST, ks, half); else issue_half(nxt, g % NST, ks - kstages, half);
+      };
+      if (ti == 0 || !stream) {
+        __builtin_amdgcn_s_waitcnt(VmCnt<0>::imm);
+        wg_barrier();                          // the ring is idle
+        issue_g(base, 0);
+        issue_g(base, 1);
+        if (staged(base + 1)) {
+          issue_g(base + 1, 0);
+          issue_g(base + 1, 1);
+          __builtin_amdgcn_s_waitcnt(VmCnt<NLOAD>::imm);
+        } else {
+          __builtin_amdgcn_s_waitcnt(VmCnt<0>::imm);
+        }
+        wg_barrier();                          // stage 0 has landed
+      }
+      for (int ks = 0; ks < kstages; ++ks) {
+        const int g = base + ks;
+        const bool s2 = staged(g + 2);
+        if (s2) issue_g(g + 2, 0);
+        wg_barrier();
+        if (s2) {
+          issue_g(g + 2, 1);
+          __builtin_amdgcn_s_waitcnt(VmCnt<NLOAD>::imm);   // stage g + 1 has landed
+        } else if (staged(g + 1)) {
+          __builtin_amdgcn_s_waitcnt(VmCnt<0>::imm);
+        }
+        wg_barrier();
+      }
+      wg_barrier();                            // the tile's last phase
+      if constexpr (EPI == EPI_SILU_FP8) wg_barrier();   // consumers' row-amax exchange
+      cur = nxt;
+      if (ti + 2 < my_tiles) nxt = make_tile(t_begin + (ti + 2) * t_step);
+    }
+    return;
   }
-  if (my_tiles > 1) {
-    nxt = make_tile(t_begin + t_step);
-    if constexpr (kFp8) load_wscales(nxt, vsw_n);
-  }
-  const uint32_t a_frag = (wm * 64 + frow) * KB;
-  const uint32_t b_frag = A_BYTES + (wn * 32 + frow) * KB;
-  const uint32_t s_frag = A_BYTES + B_BYTES + (wm * 64 + (lane >> 4) * 4) * 4;
+
+  // ================================================================== consumers
+  const int wm = wave >> 2;      // 64-row slice of the tile = consumer group
+  const int wn = wave & 3;       // 32-column slice of each half
+  // fragment reads: row (lane & 15) of a 16-row block, bytes 32*(lane>>4)..+32
+  const int frow = lane & 15;
+  const int fsw = (frow & 7) ^ (frow >> 3);
+  const int fc0 = ((2 * (lane >> 4)) ^ fsw) << 4;
+  const int fc1 = ((2 * (lane >> 4) + 1) ^ fsw) << 4;
+  const int a_frag = (wm * 64 + frow) * KB;
+  const int b_frag = A_BYTES + (wn * 32 + frow) * KB;
+  const int s_frag = A_BYTES + B_BYTES + wm * 256 + frow * 16;
+  const int w_frag = A_BYTES + B_BYTES + AS_BYTES;
 
   for (int ti = 0; ti < my_tiles; ++ti) {
-    const int base = ti * kstages;             // stream index of this tile's stage 0
-    const int e = cur.e, nb = cur.nb, rows_valid = cur.rows_valid, n0 = cur.n0;
+    const int base = ti * kstages;
+    const int nb = cur.nb, rows_valid = cur.rows_valid, n0 = cur.n0;
     const int64_t row0 = cur.row0;
     const bool half1 = cur.half1;
-    // stage g of the stream exists / is staged by the code below
-    auto staged = [&](int g) { return g < total && (stream || g < base + kstages); };
-    auto issue_g = [&](int g) {
-      const int ks = g - base;
-      if (ks < kstages) issue(cur, g % NST, ks); else issue(nxt, g % NST, ks - kstages);
-    };
-    (void)e;
 
     v4f acc[4][2][2];
 #pragma unroll
@@ -396,83 +433,54 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs p) {
         for (int j = 0; j < 2; ++j) acc[i][h][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
     if (ti == 0 || !stream) {
-      // nothing of a previous tile is still landing in the ring
-      __builtin_amdgcn_s_waitcnt(VmCnt<0>::imm);
-      __syncthreads();
-      issue_g(base);
-      if (staged(base + 1)) {
-        issue_g(base + 1);
-        __builtin_amdgcn_s_waitcnt(VmCnt<NLOAD>::imm);
-      } else {
-        __builtin_amdgcn_s_waitcnt(VmCnt<0>::imm);
-      }
-      __builtin_amdgcn_s_barrier();  // stage 0 has landed for every wave
+      wg_barrier();                            // producers: ring idle
+      wg_barrier();                            // producers: stage 0 landed
     }
-
-    // Two wave groups take turns.  Every phase ends with a workgroup
-    // barrier; in each phase one group stages and reads while the other runs
-    // the matrix products of the stage it read in the phase before, so each
-    // SIMD always has one wave feeding the matrix core and one moving data.
     // Group g reads stage ks in phase 2*ks + g and multiplies it in phase
-    // 2*ks + g + 1 (group 1 waits out phase 0, group 0 the last phase).  In
-    // its read phase for stream stage G a wave also issues its share of
-    // stage G + 2 (into the slot of G - 1, which group 1 finished reading in
-    // the phase before) and, before the closing barrier, waits for its own
-    // loads of stage G + 1 -- so neither staging issue nor waits ever sit in
-    // a matrix phase.  Stage G + 1 is first read after both groups' waits.
-    if (wm == 1) __builtin_amdgcn_s_barrier();
+    // 2*ks + g + 1 (group 1 waits out phase 0, group 0 the last phase).
+    if (wm == 1) wg_barrier();
     for (int ks = 0; ks < kstages; ++ks) {
-      const int g = base + ks;
-      // fragment reads first (no wait), then the staging loads: a wave is
-      // held at a staging load until the memory pipeline takes it, and the
-      // reads complete meanwhile
-      const uint32_t sb = ring + (g % NST) * STAGE;
-      u4 af[8], bf[8], sv[4];
-      MOE_DS_AB(af, bf, sb + a_frag + fc0, sb + a_frag + fc1, sb + b_frag + fc0, sb + b_frag + fc1);
+      const uint8_t* sb = s_ring + ((base + ks) % NST) * STAGE;
+      v8i af[4], bf[2][2];
+      i4 sa;
+      f2 sw;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) af[i] = lds_frag(sb + a_frag + i * 16 * KB, fc0, fc1);
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) bf[h][j] = lds_frag(sb + b_frag + (h * BH + j * 16) * KB, fc0, fc1);
       if constexpr (kFp8) {
-        MOE_DS_S(sv, sb + s_frag);
+        sa = *reinterpret_cast<const i4*>(sb + s_frag);
+        sw = *reinterpret_cast<const f2*>(sb + w_frag);
       } else {
-        sv[0] = sv[1] = sv[2] = sv[3] = u4{0, 0, 0, 0};
+        sa = i4{0, 0, 0, 0};
+        sw = f2{0.f, 0.f};
       }
-      if (staged(g + 2)) issue_g(g + 2);
-      if (staged(g + 2))
-        __builtin_amdgcn_s_waitcnt(VmCnt<NLOAD>::imm);
-      else if (staged(g + 1))
-        __builtin_amdgcn_s_waitcnt(VmCnt<0>::imm);
-      MOE_WAIT_BARRIER_FRAGS(af, bf, sv);
+      MOE_WAIT_BARRIER_FRAGS(af, bf, sa, sw);
       if constexpr (kFp8) {
-        const int qq = ks >> 6;
-        float sw[2];
-        sw[0] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(
-            __builtin_bit_cast(int, qq ? vsw[0][1] : vsw[0][0]), ks & 63));
-        sw[1] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(
-            __builtin_bit_cast(int, qq ? vsw[1][1] : vsw[1][0]), ks & 63));
-        // 16 independent products P, each folded in as acc += P * (sa * sw).
-        // Software-pipelined over the 8 (row sub-tile, half) pairs: the two
-        // products of pair n + 1 are issued before the fp32 folds of pair n,
-        // so the matrix core works while the vector ALU folds.
-        v4f pr[2][2];
-        auto products = [&](int n, v4f* out) {
-          const int i = n >> 1, h = n & 1;
+        // 16 products P, each folded in as acc += P * (sa * sw), one product
+        // behind: product n + 1 is issued before the fold of product n, so the
+        // matrix core works while the vector ALU folds.  Product n covers
+        // row block i = n >> 2, half h = (n >> 1) & 1, column block j = n & 1.
+        // Scheduling fences pin that order: the matrix op of product n + 1,
+        // then the fold of product n (a factor multiply for even n, four FMAs).
+        const v4f zero = {0.f, 0.f, 0.f, 0.f};
+        v4f pr[2];
+        float f = 0.f;
+        pr[0] = mma_stage<DT>(bf[0][0], af[0], zero);
 #pragma unroll
-          for (int j = 0; j < 2; ++j)
-            out[j] = mma_stage<DT>(af[2 * i], af[2 * i + 1], bf[4 * h + 2 * j],
-                                   bf[4 * h + 2 * j + 1], v4f{0.f, 0.f, 0.f, 0.f});
-        };
-        products(0, pr[0]);
-#pragma unroll
-        for (int n = 0; n < 8; ++n) {
-          if (n + 1 < 8) products(n + 1, pr[(n + 1) & 1]);
-          const int i = n >> 1, h = n & 1;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float f = __uint_as_float(sv[i][r]) * sw[h];
-#pragma unroll
-            for (int j = 0; j < 2; ++j) acc[i][h][j][r] = fmaf(pr[n & 1][j][r], f, acc[i][h][j][r]);
+        for (int n = 0; n < 16; ++n) {
+          if (n + 1 < 16) {
+            const int m = n + 1;
+            pr[m & 1] = mma_stage<DT>(bf[(m >> 1) & 1][m & 1], af[m >> 2], zero);
           }
-          // keep the issue order: 2 matrix ops, then this pair's 12 vector ops
-          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);
+          __builtin_amdgcn_sched_barrier(0);
+          const int i = n >> 2, h = (n >> 1) & 1, j = n & 1;
+          if (j == 0) f = __int_as_float(sa[i]) * sw[h];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[i][h][j][r] = fmaf(pr[n & 1][r], f, acc[i][h][j][r]);
+          __builtin_amdgcn_sched_barrier(0);
         }
       } else {
 #pragma unroll
@@ -480,39 +488,40 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs p) {
 #pragma unroll
           for (int j = 0; j < 2; ++j)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-              acc[i][h][j] = mma_stage<DT>(af[2 * i], af[2 * i + 1], bf[4 * h + 2 * j],
-                                           bf[4 * h + 2 * j + 1], acc[i][h][j]);
+            for (int i = 0; i < 4; ++i) acc[i][h][j] = mma_stage<DT>(bf[h][j], af[i], acc[i][h][j]);
       }
-      MOE_BARRIER_ACC(acc, "");
+      MOE_BARRIER_ACC(acc);
     }
-    if (wm == 0) __builtin_amdgcn_s_barrier();
+    if (wm == 0) wg_barrier();
 
-    // ---- epilogue.  Lane holds rows i*16 + (lane>>4)*4 + r, columns
-    // j*16 + (lane&15) of its 32-column slice of each half.
-    const int rbase = wm * 64 + (lane >> 4) * 4;
-    const int cbase = wn * 32 + (lane & 15);
+    // ---- epilogue.  Lane holds, for row block i, half h, column block j,
+    // activation row 64*wm + 16*i + (lane & 15) and columns
+    // 32*wn + 16*j + 4*(lane >> 4) + r of the half, r = 0..3.
+    const int mrow = wm * 64 + frow;
+    const int ncol = wn * 32 + 4 * (lane >> 4);
     if constexpr (EPI == EPI_STORE_F32 || EPI == EPI_STORE_BF16) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         if (h == 1 && !half1) continue;
         const int ncol0 = n0 + h * p.half_stride;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 4; ++i) {
+          const int row = mrow + 16 * i;
+          if (row >= rows_valid) continue;
+          const int64_t o = (row0 + row) * p.ldo + ncol0 + ncol;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int row = rbase + i * 16 + r;
-            if (row >= rows_valid) continue;
-            const int64_t o = (row0 + row) * p.ldo + ncol0;
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-              const int c = cbase + j * 16;
-              if constexpr (EPI == EPI_STORE_F32)
-                static_cast<float*>(p.out)[o + c] = acc[i][h][j][r];
-              else
-                static_cast<uint16_t*>(p.out)[o + c] = moe::f32_to_bf16(acc[i][h][j][r]);
+          for (int j = 0; j < 2; ++j) {
+            const v4f v = acc[i][h][j];
+            if constexpr (EPI == EPI_STORE_F32) {
+              *reinterpret_cast<v4f*>(static_cast<float*>(p.out) + o + 16 * j) = v;
+            } else {
+              const uint2 w = make_uint2(
+                  static_cast<uint32_t>(moe::f32_to_bf16(v[0])) | (static_cast<uint32_t>(moe::f32_to_bf16(v[1])) << 16),
+                  static_cast<uint32_t>(moe::f32_to_bf16(v[2])) | (static_cast<uint32_t>(moe::f32_to_bf16(v[3])) << 16));
+              *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + o + 16 * j) = w;
             }
           }
+        }
       }
     } else {
       // Z = SiLU(gate) * up, columns nb*128 + [0,128) of Z
@@ -525,62 +534,59 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs p) {
           for (int r = 0; r < 4; ++r) z[i][j][r] = moe::silu(acc[i][0][j][r]) * acc[i][1][j][r];
       const int64_t zcol0 = static_cast<int64_t>(nb) * BH;
       if constexpr (EPI == EPI_SILU_FP8) {
-        // per-row amax over the 128 Z columns: 2 in-lane, 16 lanes, 4 waves
+        // per-row amax over the 128 Z columns: 8 in-lane, 4 lanes, 4 waves
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 4; ++i) {
+          float m = 0.f;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            float m = fmaxf(fabsf(z[i][0][r]), fabsf(z[i][1][r]));
-            m = moe::group16_max(m);
-            if ((lane & 15) == 0) s_amax[wn][rbase + i * 16 + r] = m;
-          }
+          for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) m = fmaxf(m, fabsf(z[i][j][r]));
+          m = fmaxf(m, __shfl_xor(m, 16));
+          m = fmaxf(m, __shfl_xor(m, 32));
+          if (lane < 16) s_amax[wn][mrow + 16 * i] = m;
+        }
         __syncthreads();
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 4; ++i) {
+          const int row = mrow + 16 * i;
+          const float amax = moe::fp8_group_amax_clamp(
+              fmaxf(fmaxf(s_amax[0][row], s_amax[1][row]), fmaxf(s_amax[2][row], s_amax[3][row])));
+          const float inv = moe::fp8_group_inv(amax);
+          if (row >= rows_valid) continue;
+          uint8_t* zrow = static_cast<uint8_t*>(p.out) + (row0 + row) * p.ldo + zcol0;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int row = rbase + i * 16 + r;
-            const float amax = moe::fp8_group_amax_clamp(
-                fmaxf(fmaxf(s_amax[0][row], s_amax[1][row]), fmaxf(s_amax[2][row], s_amax[3][row])));
-            const float inv = moe::fp8_group_inv(amax);
-            if (row >= rows_valid) continue;
-            uint8_t* zrow = static_cast<uint8_t*>(p.out) + (row0 + row) * p.ldo + zcol0;
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-              zrow[cbase + j * 16] = static_cast<uint8_t>(moe::f32x2_to_e4m3(z[i][j][r] * inv, 0.f));
-            if (wn == 0 && (lane & 15) == 0)
-              p.out_scales[(row0 + row) * (p.ldo / 128) + nb] = moe::fp8_group_scale(amax);
-          }
+          for (int j = 0; j < 2; ++j)
+            *reinterpret_cast<uint32_t*>(zrow + ncol + 16 * j) = moe::f32x4_to_e4m3(
+                z[i][j][0] * inv, z[i][j][1] * inv, z[i][j][2] * inv, z[i][j][3] * inv);
+          if (wn == 0 && lane < 16)
+            p.out_scales[(row0 + row) * (p.ldo / 128) + nb] = moe::fp8_group_scale(amax);
+        }
       } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 4; ++i) {
+          const int row = mrow + 16 * i;
+          if (row >= rows_valid) continue;
+          const int64_t o = (row0 + row) * p.ldo + zcol0 + ncol;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int row = rbase + i * 16 + r;
-            if (row >= rows_valid) continue;
-            const int64_t o = (row0 + row) * p.ldo + zcol0;
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-              if constexpr (EPI == EPI_SILU_F32)
-                static_cast<float*>(p.out)[o + cbase + j * 16] = z[i][j][r];
-              else
-                static_cast<uint16_t*>(p.out)[o + cbase + j * 16] = moe::f32_to_bf16(z[i][j][r]);
+          for (int j = 0; j < 2; ++j) {
+            if constexpr (EPI == EPI_SILU_F32) {
+              *reinterpret_cast<v4f*>(static_cast<float*>(p.out) + o + 16 * j) =
+                  v4f{z[i][j][0], z[i][j][1], z[i][j][2], z[i][j][3]};
+            } else {
+              const uint2 w = make_uint2(
+                  static_cast<uint32_t>(moe::f32_to_bf16(z[i][j][0])) |
+                      (static_cast<uint32_t>(moe::f32_to_bf16(z[i][j][1])) << 16),
+                  static_cast<uint32_t>(moe::f32_to_bf16(z[i][j][2])) |
+                      (static_cast<uint32_t>(moe::f32_to_bf16(z[i][j][3])) << 16));
+              *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + o + 16 * j) = w;
             }
           }
+        }
       }
     }
-    // the next tile's first stages are already on their way
     cur = nxt;
-    if constexpr (kFp8) {
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int q = 0; q < 2; ++q) vsw[h][q] = vsw_n[h][q];
-    }
-    if (ti + 2 < my_tiles) {
-      nxt = make_tile(t_begin + (ti + 2) * t_step);
-      if constexpr (kFp8) load_wscales(nxt, vsw_n);
-    }
+    if (ti + 2 < my_tiles) nxt = make_tile(t_begin + (ti + 2) * t_step);
   }
 }
 

@@ -1,18 +1,22 @@
 """CPU model of the grouped GEMM's staging protocol (gemm.hip, K loop).
 
-The kernel keeps three LDS stages in a ring and splits its 8 waves into two
-groups that alternate read and matrix phases, one phase apart; every phase
-ends with a workgroup barrier.  A workgroup's tiles form one stream of
-stages; in its read phase for stream stage G a wave issues its
-direct-to-LDS loads of stage G + 2 (possibly the next tile's) and, before the
-closing barrier, waits (vmcnt) until its own loads of stage G + 1 have
-landed.  This test replays that program order for both groups, for 1, 2 and
-5 tiles of many stage counts, and checks the two properties the kernel
-relies on:
+The kernel keeps three LDS stages in a ring.  Four producer waves only
+issue direct-to-LDS loads; eight consumer waves in two groups only read
+LDS fragments and multiply, alternating read and matrix phases one phase
+apart.  Every phase ends with a workgroup barrier taken by all twelve waves.
+A workgroup's tiles form one stream of stages.  In the two phases of stream
+stage G a producer issues its loads of stage G + 2 (first half, barrier,
+second half) and then waits (vmcnt) until its loads of stage G + 1 have
+landed.  Producer 0 issues one extra load per stage (the FP8 weight scales),
+first.  This test replays that program order for every role, for 1, 2 and
+5 tiles of many stage counts, and checks the properties the kernel relies
+on:
 
-* every read of stage s by either group comes after a barrier that follows
-  every wave's wait for stage s;
-* a slot is only re-staged after every read of the stage it held.
+* every role passes the same number of barriers;
+* every read of stage s by either consumer group comes after a barrier that
+  follows every producer's wait for all of its loads of s;
+* a slot is only re-staged after a barrier that follows every read of the
+  stage it held.
 
 Loads complete in issue order (vmcnt(n) = all but the last n loads landed)."""
 import pytest
@@ -20,95 +24,163 @@ import pytest
 NST = 3          # LDS ring depth
 
 
-def wave_program(group, K, tiles=1):
-    """Program order of one wave over `tiles` tiles of K stages each.  The
-    stages of all tiles form one stream (stage g = K stage g % K of tile
-    g // K, slot g % NST); with K >= 2 the next tile's first stages are
-    staged during the current tile, otherwise each tile refills the ring."""
+def _stream(K, tiles):
     total = tiles * K
     stream = K >= 2
+
+    def staged_fn(base):
+        return lambda g: g < total and (stream or g < base + K)
+    return stream, staged_fn
+
+
+def consumer_program(group, K, tiles=1, fp8_epilogue=True):
+    stream, _ = _stream(K, tiles)
     ev = []
     for ti in range(tiles):
         base = ti * K
-
-        def staged(g):
-            return g < total and (stream or g < base + K)
-
         if ti == 0 or not stream:
-            ev += [("wait", 0), ("bar", None)]         # ring idle
-            ev.append(("issue", base))
-            if staged(base + 1):
-                ev += [("issue", base + 1), ("wait", 1)]
-            else:
-                ev.append(("wait", 0))
-            ev.append(("bar", None))
+            ev += [("bar", None), ("bar", None)]      # producers fill stage 0
         if group == 1:
             ev.append(("bar", None))                  # group 1 sits out the tile's phase 0
         for ks in range(K):
-            g = base + ks
-            if staged(g + 2):
-                ev.append(("issue", g + 2))
-            ev.append(("read", g))
-            if staged(g + 2):
-                ev.append(("wait", 1))
-            elif staged(g + 1):
-                ev.append(("wait", 0))
-            ev.append(("bar", None))                  # end of read phase
+            ev.append(("read", base + ks))
+            ev.append(("bar", None))                  # end of read phase (reads complete)
             ev.append(("bar", None))                  # end of matrix phase
         if group == 0:
             ev.append(("bar", None))                  # group 0 sits out the last phase
-        ev.append(("bar", None))                      # epilogue barrier (FP8 Z amax)
+        if fp8_epilogue:
+            ev.append(("bar", None))                  # row-amax exchange of the FP8 Z epilogue
     return ev
 
 
-def replay(K, tiles=1):
-    info = {}
-    for g in (0, 1):
-        b, issued, landed_at, reads, issues = 0, [], {}, [], []
-        for kind, a in wave_program(g, K, tiles):
-            if kind == "bar":
-                b += 1
-            elif kind == "issue":
-                issued.append(a)
-                issues.append((a, b))
-            elif kind == "wait":
-                for s in (issued[:len(issued) - a] if a else issued):
-                    landed_at.setdefault(s, b)
+def producer_program(K, tiles=1, fp8=True, first=False, fp8_epilogue=True):
+    """One producer wave.  FP8: 7 + 6 loads per stage (+1 weight-scale load
+    issued first by producer 0); otherwise 6 + 6."""
+    stream, staged_fn = _stream(K, tiles)
+    halves = (7, 6) if fp8 else (6, 6)
+    nload = sum(halves)
+    ev = []
+
+    def issue(g, half):
+        n = halves[half] + (1 if (fp8 and first and half == 0) else 0)
+        return [("issue", g)] * n
+
+    for ti in range(tiles):
+        base = ti * K
+        staged = staged_fn(base)
+        if ti == 0 or not stream:
+            ev += [("wait", 0), ("bar", None)]
+            ev += issue(base, 0) + issue(base, 1)
+            if staged(base + 1):
+                ev += issue(base + 1, 0) + issue(base + 1, 1) + [("wait", nload)]
             else:
-                reads.append((a, b))
-        info[g] = (b, landed_at, reads, issues)
-    return info
+                ev.append(("wait", 0))
+            ev.append(("bar", None))
+        for ks in range(K):
+            g = base + ks
+            s2 = staged(g + 2)
+            if s2:
+                ev += issue(g + 2, 0)
+            ev.append(("bar", None))
+            if s2:
+                ev += issue(g + 2, 1) + [("wait", nload)]
+            elif staged(g + 1):
+                ev.append(("wait", 0))
+            ev.append(("bar", None))
+        ev.append(("bar", None))                      # the tile's last phase
+        if fp8_epilogue:
+            ev.append(("bar", None))
+    return ev
 
 
+def replay_consumer(prog):
+    b, reads = 0, []
+    for kind, a in prog:
+        if kind == "bar":
+            b += 1
+        elif kind == "read":
+            reads.append((a, b))
+    return b, reads
+
+
+def replay_producer(prog):
+    """-> (barriers, {stage: barrier count at the wait that landed all of
+    its loads}, [(stage, barrier count at issue)])"""
+    b, issued, landed, issues = 0, [], 0, []
+    landed_at = {}
+    for kind, a in prog:
+        if kind == "bar":
+            b += 1
+        elif kind == "issue":
+            issued.append(a)
+            issues.append((a, b))
+        else:
+            landed = max(landed, len(issued) - a)
+            done = issued[:landed]
+            for s in set(done):
+                if s not in landed_at and issued.count(s) == done.count(s):
+                    landed_at[s] = b
+    return b, landed_at, issues
+
+
+def check(K, tiles, fp8, fp8_epilogue, programs=None):
+    progs = programs or {
+        "c0": consumer_program(0, K, tiles, fp8_epilogue),
+        "c1": consumer_program(1, K, tiles, fp8_epilogue),
+        "p0": producer_program(K, tiles, fp8, True, fp8_epilogue),
+        "p1": producer_program(K, tiles, fp8, False, fp8_epilogue),
+    }
+    cons = {k: replay_consumer(v) for k, v in progs.items() if k[0] == "c"}
+    prod = {k: replay_producer(v) for k, v in progs.items() if k[0] == "p"}
+    bars = {k: v[0] for k, v in cons.items()} | {k: v[0] for k, v in prod.items()}
+    assert len(set(bars.values())) == 1, ("barrier counts differ", bars)
+    for ck, (_, reads) in cons.items():
+        for s, b in reads:
+            for pk, (_, landed_at, _) in prod.items():
+                lb = landed_at.get(s)
+                assert lb is not None and lb < b, (K, ck, s, pk, lb, b)
+    for pk, (_, _, issues) in prod.items():
+        for s, b in issues:
+            if s >= NST:
+                for ck, (_, reads) in cons.items():
+                    for s2, b2 in reads:
+                        if s2 == s - NST:
+                            assert b2 < b, (K, pk, s, ck, b2, b)
+
+
+@pytest.mark.parametrize("fp8,fp8_epilogue", [(True, True), (True, False), (False, False)])
 @pytest.mark.parametrize("tiles", [1, 2, 5])
 @pytest.mark.parametrize("K", list(range(1, 40)) + [56, 64, 112, 128])
-def test_staging_protocol(K, tiles):
-    info = replay(K, tiles)
-    assert info[0][0] == info[1][0], "both groups must pass the same number of barriers"
-    for g in (0, 1):
-        for s, b in info[g][2]:
-            for g2 in (0, 1):
-                lb = info[g2][1].get(s)
-                assert lb is not None and lb < b, (K, g, s, g2)
-        for s, b in info[g][3]:
-            if s >= NST:
-                for g2 in (0, 1):
-                    for s2, b2 in info[g2][2]:
-                        if s2 == s - NST:
-                            assert b2 < b, (K, g, s, g2)
+def test_staging_protocol(K, tiles, fp8, fp8_epilogue):
+    check(K, tiles, fp8, fp8_epilogue)
 
 
 def test_protocol_model_detects_a_missing_wait():
-    """The checker itself fails when a wave skips its wait for stage ks + 1."""
-    global wave_program
-    orig = wave_program
+    """The checker fails when a producer skips its wait for stage G + 1."""
+    K, tiles = 8, 2
+    p1 = producer_program(K, tiles, True, False)
+    i = next(n for n, e in enumerate(p1) if e == ("wait", 13) and n > 40)
+    broken = {
+        "c0": consumer_program(0, K, tiles), "c1": consumer_program(1, K, tiles),
+        "p0": producer_program(K, tiles, True, True), "p1": p1[:i] + p1[i + 1:],
+    }
+    with pytest.raises(AssertionError):
+        check(K, tiles, True, True, broken)
 
-    def broken(group, K, tiles=1):
-        return [e for e in orig(group, K, tiles) if not (group == 1 and e == ("wait", 1))]
 
-    try:
-        wave_program = broken
-        with pytest.raises(AssertionError):
-            test_staging_protocol(8, 2)
-    finally:
-        wave_program = orig
+def test_protocol_model_detects_early_restaging():
+    """The checker fails when a producer issues stage G + 2 one phase early."""
+    K, tiles = 8, 1
+    p0 = producer_program(K, tiles, True, True)
+    # move the first in-loop barrier behind the second half of stage 4
+    # (stage 4 re-stages the slot of stage 1, which group 1 is still reading)
+    bars = [n for n, e in enumerate(p0) if e == ("bar", None)]
+    n = bars[3]                                   # closes group 0's read of stage 1
+    broken_p0 = p0[:n] + p0[n + 1:]
+    broken_p0.insert(len(broken_p0) - 1, ("bar", None))
+    broken = {
+        "c0": consumer_program(0, K, tiles), "c1": consumer_program(1, K, tiles),
+        "p0": broken_p0, "p1": producer_program(K, tiles, True, False),
+    }
+    with pytest.raises(AssertionError):
+        check(K, tiles, True, True, broken)
