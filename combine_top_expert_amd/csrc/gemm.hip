@@ -459,27 +459,29 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs p) {
       }
       MOE_WAIT_BARRIER_FRAGS(af, bf, sa, sw);
       if constexpr (kFp8) {
-        // 16 products P, each folded in as acc += P * (sa * sw), one product
-        // behind: product n + 1 is issued before the fold of product n, so the
-        // matrix core works while the vector ALU folds.  Product n covers
-        // row block i = n >> 2, half h = (n >> 1) & 1, column block j = n & 1.
-        // Scheduling fences pin that order: the matrix op of product n + 1,
-        // then the fold of product n (a factor multiply for even n, four FMAs).
+        // 16 products P, each folded in as acc += P * (sa * sw) while the
+        // matrix core works on later products.  Product n covers row block
+        // i = n >> 2, half h = (n >> 1) & 1, column block j = n & 1.
+        // Two products ahead: the fold of product n follows the matrix op of
+        // product n + 2, far enough behind product n for its result to be
+        // ready without a stall (one product ahead, every fold waits on the
+        // matrix op issued just before it).  Scheduling fences pin the order.
         const v4f zero = {0.f, 0.f, 0.f, 0.f};
-        v4f pr[2];
+        v4f pr[3];
         float f = 0.f;
         pr[0] = mma_stage<DT>(bf[0][0], af[0], zero);
+        pr[1] = mma_stage<DT>(bf[0][1], af[0], zero);
 #pragma unroll
         for (int n = 0; n < 16; ++n) {
-          if (n + 1 < 16) {
-            const int m = n + 1;
-            pr[m & 1] = mma_stage<DT>(bf[(m >> 1) & 1][m & 1], af[m >> 2], zero);
+          if (n + 2 < 16) {
+            const int m = n + 2;
+            pr[m % 3] = mma_stage<DT>(bf[(m >> 1) & 1][m & 1], af[m >> 2], zero);
           }
           __builtin_amdgcn_sched_barrier(0);
           const int i = n >> 2, h = (n >> 1) & 1, j = n & 1;
           if (j == 0) f = __int_as_float(sa[i]) * sw[h];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) acc[i][h][j][r] = fmaf(pr[n & 1][r], f, acc[i][h][j][r]);
+          for (int r = 0; r < 4; ++r) acc[i][h][j][r] = fmaf(pr[n % 3][r], f, acc[i][h][j][r]);
           __builtin_amdgcn_sched_barrier(0);
         }
       } else {

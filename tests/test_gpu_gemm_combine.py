@@ -21,8 +21,10 @@ from workloads import get_config, make_routing, make_share_buffer, make_workload
 
 pytestmark = pytest.mark.gpu
 
+# the last three: few experts with hundreds of rows each (many row tiles per
+# expert), odd and single-stage K loops
 GEMM_CASES = ["toy_fp32", "share_bf16", "toy_bf16_fp8w", "decode_fp8_small", "prefill_fp8_small",
-              "skewed_bf16_small"]
+              "skewed_bf16_small", "manyrow_bf16_small", "manyrow_fp8_small", "manyrow_fp32_small"]
 
 
 @pytest.fixture(scope="module")

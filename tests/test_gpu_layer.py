@@ -67,7 +67,8 @@ def check(y, ref, tag=""):
 
 @pytest.mark.parametrize("fused", [True, False])
 @pytest.mark.parametrize("name", ["toy_fp32", "share_bf16", "toy_bf16_fp8w", "decode_fp8_small",
-                                  "prefill_fp8_small", "skewed_bf16_small"])
+                                  "prefill_fp8_small", "skewed_bf16_small", "manyrow_bf16_small",
+                                  "manyrow_fp8_small", "manyrow_fp32_small"])
 def test_layer_small_all_tokens(ep, name, fused):
     announce("layer", name, "fused" if fused else "unfused")
     wl = make_workload(name)

@@ -113,6 +113,21 @@ CONFIGS.update({
     "toy_bf16_fp8w": CONFIGS["toy_fp32"].scaled(name="toy_bf16_fp8w", act="bf16", wdt="fp8"),
 })
 
+# Reduced shapes with a few experts holding hundreds of rows each: several
+# full GEMM row tiles per expert, ragged tails and near-empty experts
+# (Zipf-biased routing); odd and single-stage K loops (FP8: H=128 is one
+# 128-byte stage, I=384 three).
+CONFIGS.update({
+    "manyrow_bf16_small": CONFIGS["skewed_bf16"].scaled(
+        name="manyrow_bf16_small", T=1024, K=2, E=4, L=4, H=384, I=256),
+    "manyrow_fp8_small": CONFIGS["prefill_fp8"].scaled(
+        name="manyrow_fp8_small", T=512, K=4, E=8, L=4, H=128, I=384, R=640,
+        bias="zipf", bias_alpha=1.2),
+    "manyrow_fp32_small": CONFIGS["toy_fp32"].scaled(
+        name="manyrow_fp32_small", T=384, K=2, E=4, L=4, R=384, routing="softmax",
+        bias="zipf", bias_alpha=1.2),
+})
+
 
 def get_config(name: str) -> MoEConfig:
     return CONFIGS[name]
