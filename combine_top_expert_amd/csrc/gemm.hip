@@ -325,6 +325,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs p) {
         const_cast<float*>(p.As), 0, static_cast<int>(p.rows_cap * kgroups * 4), kRsrcWord3) : rA;
     const __amdgpu_buffer_rsrc_t rWs = kFp8 ? __builtin_amdgcn_make_buffer_rsrc(
         const_cast<float*>(p.Ws), 0, p.L * (p.N / 128) * kgroups * 4, kRsrcWord3) : rA;
+    // zero records: every access is out of range, reads zeros, moves nothing
+    const __amdgpu_buffer_rsrc_t rNone = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p.A), 0, 0, kRsrcWord3);
     typedef __attribute__((address_space(3))) void* lds_void;
 
     // half 0 / half 1 of this producer's loads of K stage ks of tile c into
@@ -343,7 +345,12 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs p) {
 #pragma unroll
       for (int jj = 0; jj < 2; ++jj) {
         const int j = 2 * half + jj;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_void)(st + (32 * pw + 8 * j) * KB), 16,
+        // 8-row groups wholly past the tile's valid rows (an expert's tail,
+        // most of a decode tile) go to the empty resource: the load still
+        // counts (the vmcnt bookkeeping stays fixed) but touches no memory;
+        // those rows' results are never stored
+        const bool live = 32 * pw + 8 * j < c.rows_valid;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(live ? rA : rNone, (lds_void)(st + (32 * pw + 8 * j) * KB), 16,
                                                  (j & 1) ? voff_o : voff_e,
                                                  a_off + static_cast<int>(8 * j * lda), 0, 0);
       }
