@@ -3,12 +3,12 @@
 // "DeepEP 架构与实现笔记" §9.4 and §11).
 //
 // One wavefront per token.  The token's routes are read once (lane k =
-// route k); its row is read from HBM once, with up to 16 16-byte chunks per
-// lane in flight, quantised once (the code of a row does not depend on which
-// expert receives it), and stored to each of its local slots.  A
-// 128-column FP8 group is covered by 16 lanes (bf16 input) or 32 lanes
-// (fp32 input); its amax is a butterfly max inside those lanes.  Tokens
-// without a local route read nothing.
+// route k); its row is read from HBM once, with up to 256 bytes per lane in
+// flight, quantised once (the code of a row does not depend on which expert
+// receives it), and stored to each of its local slots.  A 128-column FP8
+// group is covered by 8 lanes of 16 values (bf16 input, 16-byte code stores)
+// or 32 lanes of 4 values (fp32 input); its amax is a butterfly max inside
+// those lanes.  Tokens without a local route read nothing.
 
 #include "moe_common.h"
 
@@ -118,6 +118,70 @@ __global__ __launch_bounds__(kThreads) void permute_kernel(const TIn* __restrict
   }
 }
 
+// bf16 -> block FP8, the main path: each lane converts 16 consecutive
+// values (two 16-byte loads) into one 16-byte store of codes per local slot,
+// so a 128-column group is 8 lanes and a wave stores 1 KB per instruction.
+constexpr int kUnroll2 = 8;          // 32-byte lane units in flight (a 8192-column row)
+
+__global__ __launch_bounds__(kThreads) void permute_bf16_fp8_kernel(const uint16_t* __restrict__ x, int T,
+                                                                   int K, int H,
+                                                                   const int32_t* __restrict__ slot_of,
+                                                                   int64_t rows_cap, uint8_t* __restrict__ buf,
+                                                                   float* __restrict__ scales) {
+  const int wave = threadIdx.x / MOE_WAVE;
+  const int lane = moe::lane_id();
+  const int t = blockIdx.x * kTokPerBlock + wave;
+  if (t >= T) return;
+  const int s_l = lane < K ? slot_of[static_cast<int64_t>(t) * K + lane] : -1;
+  const uint64_t routes = __ballot(s_l >= 0 && s_l < rows_cap);
+  if (!routes) return;
+
+  const int nunit = H / 16;                       // 32-byte units of the input row
+  const uint4* xrow = reinterpret_cast<const uint4*>(x + static_cast<int64_t>(t) * H);
+  const int groups = H / 128;
+  for (int d0 = 0; d0 < nunit; d0 += MOE_WAVE * kUnroll2) {
+    uint4 raw[kUnroll2][2];
+#pragma unroll
+    for (int u = 0; u < kUnroll2; ++u) {
+      const int d = d0 + u * MOE_WAVE + lane;
+      const bool live = d < nunit;
+      raw[u][0] = live ? moe::load_nt16(xrow + 2 * d) : make_uint4(0, 0, 0, 0);
+      raw[u][1] = live ? moe::load_nt16(xrow + 2 * d + 1) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll2; ++u) {
+      const int dw = d0 + u * MOE_WAVE;           // wave-uniform unit base
+      if (dw >= nunit) break;
+      const int d = dw + lane;
+      const bool live = d < nunit;
+      float f[16];
+      Vec<uint16_t>::to_f32(raw[u][0], f);
+      Vec<uint16_t>::to_f32(raw[u][1], f + 8);
+      float amax = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(f[i]));
+      amax = fmaxf(amax, __shfl_xor(amax, 1));
+      amax = fmaxf(amax, __shfl_xor(amax, 2));
+      amax = fmaxf(amax, __shfl_xor(amax, 4));
+      amax = moe::fp8_group_amax_clamp(amax);
+      const float inv = moe::fp8_group_inv(amax);
+      uint4 codes;
+      codes.x = moe::f32x4_to_e4m3(f[0] * inv, f[1] * inv, f[2] * inv, f[3] * inv);
+      codes.y = moe::f32x4_to_e4m3(f[4] * inv, f[5] * inv, f[6] * inv, f[7] * inv);
+      codes.z = moe::f32x4_to_e4m3(f[8] * inv, f[9] * inv, f[10] * inv, f[11] * inv);
+      codes.w = moe::f32x4_to_e4m3(f[12] * inv, f[13] * inv, f[14] * inv, f[15] * inv);
+      const float scale = moe::fp8_group_scale(amax);
+      const int g = d >> 3;
+      for (uint64_t m = routes; m; m &= m - 1) {
+        const int s = __builtin_amdgcn_readlane(s_l, __builtin_ctzll(m));
+        if (!live) continue;
+        moe::store_nt16(buf + static_cast<int64_t>(s) * H + d * 16, codes);
+        if ((lane & 7) == 0) scales[static_cast<int64_t>(s) * groups + g] = scale;
+      }
+    }
+  }
+}
+
 }  // namespace
 
 extern "C" moe_status moe_permute(const void* x, moe_dtype x_dt, int T, int K, int H,
@@ -136,7 +200,7 @@ extern "C" moe_status moe_permute(const void* x, moe_dtype x_dt, int T, int K, i
   if (x_dt == MOE_BF16) {
     auto* xi = static_cast<const uint16_t*>(x);
     if (buf_dt == MOE_FP8_E4M3)
-      permute_kernel<uint16_t, true><<<grid, kThreads, 0, stream>>>(xi, T, K, H, slot_of, rows_cap, b, buf_scales);
+      permute_bf16_fp8_kernel<<<grid, kThreads, 0, stream>>>(xi, T, K, H, slot_of, rows_cap, b, buf_scales);
     else
       permute_kernel<uint16_t, false><<<grid, kThreads, 0, stream>>>(xi, T, K, H, slot_of, rows_cap, b, nullptr);
   } else {
