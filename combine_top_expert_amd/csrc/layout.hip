@@ -8,7 +8,7 @@
 // per-expert atomic counter gives an arrival-order permutation of the same
 // rows; ordering by i instead makes the layout unique.
 //
-// Three launches:
+// Passes:
 //   1. count : every block takes PAIRS_PER_BLOCK consecutive routes and
 //              histograms them per local expert in LDS -> ws_hist[blk][L].
 //   2. scan  : one block turns the histograms into exclusive prefixes over
@@ -19,6 +19,9 @@
 //              from ballot + mbcnt; chunk ranks are scanned in LDS and added
 //              to the block prefix.  Writes slot_of and row_src, and marks
 //              padding rows of row_src with -1.
+// Launches: one (count, scan and place fused) when the routes fit one
+// block's share; two (count, then scan fused into place: each block reads
+// the whole histogram table) while that table is small; otherwise three.
 
 #include "moe_common.h"
 
@@ -30,6 +33,9 @@ constexpr int kChunksPerBlock = 16;                    // 64-route chunks
 constexpr int kPairsPerBlock = kChunksPerBlock * MOE_WAVE;  // 1024
 constexpr int kScanThreads = 1024;
 constexpr int kMaxL = 1024;
+// largest per-block histogram table (blocks x local experts) that each
+// place block reads whole instead of a separate scan launch
+constexpr int64_t kFusedTable = 16384;
 
 struct LayoutArgs {
   const int32_t* ids;
@@ -139,7 +145,8 @@ __global__ __launch_bounds__(kScanThreads) void layout_scan_kernel(LayoutArgs a)
   __syncthreads();
   // 4. offsets
   if (a.R > 0) {
-    if (e <= L) a.offsets[e] = e * a.R;
+    if (e < L) a.offsets[e] = e * a.R;
+    if (e == 0) a.offsets[L] = L * a.R;       // L may equal the block size
   } else {
     block_inclusive_scan(vals, tmp, L);
     if (e < L) a.offsets[e + 1] = vals[e];
@@ -159,129 +166,253 @@ __global__ __launch_bounds__(kScanThreads) void layout_scan_kernel(LayoutArgs a)
   }
 }
 
-__global__ __launch_bounds__(kThreads) void layout_place_kernel(LayoutArgs a) {
-  __shared__ int chunk_cnt[kChunksPerBlock][64];  // per chunk, per expert (L <= 64 path)
-  __shared__ int base[kMaxL];
+__shared__ int s_chunk_cnt[kChunksPerBlock][64];  // per chunk, per expert (L <= 64 path)
+
+// Block blk's routes -> slot_of / row_src.  base[e]: routes of expert e in
+// earlier blocks; off[e]: first row of expert e.  Block-uniform call (it
+// synchronises the block).
+__device__ void place_routes(const LayoutArgs& a, int blk, int* base, const int* off) {
   const int L = a.L;
   const int wave = threadIdx.x / MOE_WAVE;
   const int lane = moe::lane_id();
-  const int blk = blockIdx.x;
+  const int64_t pbase = static_cast<int64_t>(blk) * kPairsPerBlock;
 
-  if (blk < a.n_blocks) {
-    const int32_t* pre = a.ws_hist + static_cast<int64_t>(blk) * L;
-    for (int e = threadIdx.x; e < L; e += kThreads) base[e] = pre[e];
-    const int64_t pbase = static_cast<int64_t>(blk) * kPairsPerBlock;
-
-    // Per-chunk rank among equal experts.  For L <= 64 the per-chunk counts
-    // live in LDS and one scan over chunks follows; for larger L the block's
-    // chunks are processed in order with a running per-expert counter.
-    int e_of[kChunksPerBlock / kWaves];
-    int rank[kChunksPerBlock / kWaves];
-    if (L <= 64) {
-      for (int i = threadIdx.x; i < kChunksPerBlock * 64; i += kThreads)
-        (&chunk_cnt[0][0])[i] = 0;
-      __syncthreads();
-      for (int r = 0; r < kChunksPerBlock / kWaves; ++r) {
-        const int c = r * kWaves + wave;
+  // Per-chunk rank among equal experts.  For L <= 64 the per-chunk counts
+  // live in LDS and one scan over chunks follows; for larger L the block's
+  // chunks are processed in order with a running per-expert counter.
+  int e_of[kChunksPerBlock / kWaves];
+  int rank[kChunksPerBlock / kWaves];
+  if (L <= 64) {
+    for (int i = threadIdx.x; i < kChunksPerBlock * 64; i += kThreads)
+      (&s_chunk_cnt[0][0])[i] = 0;
+    __syncthreads();
+    for (int r = 0; r < kChunksPerBlock / kWaves; ++r) {
+      const int c = r * kWaves + wave;
+      bool bad = false;
+      const int e = local_expert(a, pbase + c * MOE_WAVE + lane, &bad);
+      uint64_t left = moe::ballot(e >= 0);
+      int my_rank = 0;
+      while (left) {
+        const int leader = __builtin_ctzll(left);
+        const int le = __builtin_amdgcn_readlane(e, leader);
+        const uint64_t m = moe::ballot(e == le);
+        if (e == le) {
+          my_rank = moe::mbcnt(m);
+          if (lane == leader) s_chunk_cnt[c][le] = __builtin_popcountll(m);
+        }
+        left &= ~m;
+      }
+      e_of[r] = e;
+      rank[r] = my_rank;
+    }
+    __syncthreads();
+    // exclusive scan over the block's chunks, per expert
+    for (int e = threadIdx.x; e < L; e += kThreads) {
+      int run = 0;
+      for (int c = 0; c < kChunksPerBlock; ++c) {
+        int v = s_chunk_cnt[c][e];
+        s_chunk_cnt[c][e] = run;
+        run += v;
+      }
+    }
+    __syncthreads();
+    for (int r = 0; r < kChunksPerBlock / kWaves; ++r) {
+      const int c = r * kWaves + wave;
+      const int64_t p = pbase + c * MOE_WAVE + lane;
+      if (p >= a.n_pairs) continue;
+      const int e = e_of[r];
+      int slot = -1;
+      if (e >= 0) {
+        const int s = base[e] + s_chunk_cnt[c][e] + rank[r];
+        if (a.R <= 0 || s < a.R) {
+          const int q = off[e] + s;
+          if (q < a.rows_cap) {
+            slot = q;
+            a.row_src[q] = static_cast<int32_t>(p);
+          }
+        }
+      }
+      a.slot_of[p] = slot;
+    }
+  } else {
+    // L > 64: chunks in order; each chunk's leaders bump the running count
+    // in base[] after every lane of that chunk has read it.
+    __syncthreads();
+    for (int c = 0; c < kChunksPerBlock; ++c) {
+      const int64_t p = pbase + c * MOE_WAVE + lane;
+      int e = -1;
+      int my_rank = 0;
+      uint64_t mask_of_mine = 0;
+      if (wave == 0) {
         bool bad = false;
-        const int e = local_expert(a, pbase + c * MOE_WAVE + lane, &bad);
+        e = local_expert(a, p, &bad);
         uint64_t left = moe::ballot(e >= 0);
-        int my_rank = 0;
         while (left) {
           const int leader = __builtin_ctzll(left);
           const int le = __builtin_amdgcn_readlane(e, leader);
           const uint64_t m = moe::ballot(e == le);
-          if (e == le) {
-            my_rank = moe::mbcnt(m);
-            if (lane == leader) chunk_cnt[c][le] = __builtin_popcountll(m);
-          }
+          if (e == le) { my_rank = moe::mbcnt(m); mask_of_mine = m; }
           left &= ~m;
         }
-        e_of[r] = e;
-        rank[r] = my_rank;
-      }
-      __syncthreads();
-      // exclusive scan over the block's chunks, per expert
-      for (int e = threadIdx.x; e < L; e += kThreads) {
-        int run = 0;
-        for (int c = 0; c < kChunksPerBlock; ++c) {
-          int v = chunk_cnt[c][e];
-          chunk_cnt[c][e] = run;
-          run += v;
-        }
-      }
-      __syncthreads();
-      for (int r = 0; r < kChunksPerBlock / kWaves; ++r) {
-        const int c = r * kWaves + wave;
-        const int64_t p = pbase + c * MOE_WAVE + lane;
-        if (p >= a.n_pairs) continue;
-        const int e = e_of[r];
         int slot = -1;
         if (e >= 0) {
-          const int s = base[e] + chunk_cnt[c][e] + rank[r];
+          const int s = base[e] + my_rank;
           if (a.R <= 0 || s < a.R) {
-            const int q = a.offsets[e] + s;
+            const int q = off[e] + s;
             if (q < a.rows_cap) {
               slot = q;
               a.row_src[q] = static_cast<int32_t>(p);
             }
           }
         }
-        a.slot_of[p] = slot;
+        if (p < a.n_pairs) a.slot_of[p] = slot;
       }
-    } else {
-      // L > 64: chunks in order; each chunk's leaders bump the running count
-      // in base[] after every lane of that chunk has read it.
       __syncthreads();
-      for (int c = 0; c < kChunksPerBlock; ++c) {
-        const int64_t p = pbase + c * MOE_WAVE + lane;
-        int e = -1;
-        int my_rank = 0;
-        uint64_t mask_of_mine = 0;
-        if (wave == 0) {
-          bool bad = false;
-          e = local_expert(a, p, &bad);
-          uint64_t left = moe::ballot(e >= 0);
-          while (left) {
-            const int leader = __builtin_ctzll(left);
-            const int le = __builtin_amdgcn_readlane(e, leader);
-            const uint64_t m = moe::ballot(e == le);
-            if (e == le) { my_rank = moe::mbcnt(m); mask_of_mine = m; }
-            left &= ~m;
-          }
-          int slot = -1;
-          if (e >= 0) {
-            const int s = base[e] + my_rank;
-            if (a.R <= 0 || s < a.R) {
-              const int q = a.offsets[e] + s;
-              if (q < a.rows_cap) {
-                slot = q;
-                a.row_src[q] = static_cast<int32_t>(p);
-              }
-            }
-          }
-          if (p < a.n_pairs) a.slot_of[p] = slot;
-        }
-        __syncthreads();
-        if (wave == 0 && e >= 0 && moe::mbcnt(mask_of_mine) == 0)
-          base[e] += __builtin_popcountll(mask_of_mine);
-        __syncthreads();
-      }
+      if (wave == 0 && e >= 0 && moe::mbcnt(mask_of_mine) == 0)
+        base[e] += __builtin_popcountll(mask_of_mine);
+      __syncthreads();
     }
   }
+}
 
-  // padding rows of row_src -> -1 (valid rows are written above)
+// padding rows of row_src -> -1 (valid rows are written by place_routes)
+__device__ void fill_padding(const LayoutArgs& a, int blk, const int* cnt, const int* off) {
   const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
   for (int64_t q = static_cast<int64_t>(blk) * kThreads + threadIdx.x; q < a.rows_cap; q += stride) {
     bool pad;
     if (a.R > 0) {
       const int e = static_cast<int>(q / a.R);
-      pad = (q - static_cast<int64_t>(e) * a.R) >= a.counts[e];
+      pad = (q - static_cast<int64_t>(e) * a.R) >= cnt[e];
     } else {
-      pad = q >= a.offsets[L];
+      pad = q >= off[a.L];
     }
     if (pad) a.row_src[q] = -1;
   }
+}
+
+__global__ __launch_bounds__(kThreads) void layout_place_kernel(LayoutArgs a) {
+  __shared__ int base[kMaxL];
+  const int blk = blockIdx.x;
+  if (blk < a.n_blocks) {
+    const int32_t* pre = a.ws_hist + static_cast<int64_t>(blk) * a.L;
+    for (int e = threadIdx.x; e < a.L; e += kThreads) base[e] = pre[e];
+    place_routes(a, blk, base, a.offsets);
+  }
+  fill_padding(a, blk, a.counts, a.offsets);
+}
+
+// exclusive scan of v[0..n) in place by the block's threads (n <= kMaxL);
+// returns the total.  Block-uniform call.
+__device__ int block_exclusive_scan(int* v, int n, int* part) {
+  const int t = threadIdx.x;
+  const int per = (n + kThreads - 1) / kThreads;
+  const int i0 = t * per;
+  int s = 0;
+  for (int i = i0; i < min(i0 + per, n); ++i) s += v[i];
+  part[t] = s;
+  __syncthreads();
+  for (int d = 1; d < kThreads; d <<= 1) {
+    const int x = t >= d ? part[t - d] : 0;
+    __syncthreads();
+    part[t] += x;
+    __syncthreads();
+  }
+  int run = part[t] - s;
+  for (int i = i0; i < min(i0 + per, n); ++i) {
+    const int x = v[i];
+    v[i] = run;
+    run += x;
+  }
+  const int total = part[kThreads - 1];
+  __syncthreads();
+  return total;
+}
+
+// Count, scan and place in one launch.  kSingle: all routes fit one block's
+// share and every block histograms them itself (no workspace); otherwise
+// every block derives its prefix and the expert totals from the count
+// pass's per-block histograms.  Each block rebuilds counts, offsets and
+// tile offsets in LDS; block 0 also writes them out.
+template <bool kSingle>
+__global__ __launch_bounds__(kThreads) void layout_fused_kernel(LayoutArgs a) {
+  __shared__ int s_base[kMaxL];
+  __shared__ int s_cnt[kMaxL];
+  __shared__ int s_off[kMaxL + 1];
+  __shared__ int s_tile[kMaxL + 1];
+  __shared__ int s_part[kThreads];
+  __shared__ int s_flags, s_dropped;
+  const int L = a.L;
+  const int blk = blockIdx.x;
+  for (int e = threadIdx.x; e < L; e += kThreads) {
+    s_base[e] = 0;
+    s_cnt[e] = 0;
+  }
+  if (threadIdx.x == 0) {
+    s_flags = 0;
+    s_dropped = 0;
+  }
+  __syncthreads();
+  bool bad = false;
+  if constexpr (kSingle) {
+    for (int64_t i = threadIdx.x; i < a.n_pairs; i += kThreads) {
+      const int e = local_expert(a, i, &bad);
+      if (e >= 0) atomicAdd(&s_cnt[e], 1);
+    }
+  } else {
+    // the whole table through LDS: one coalesced sweep, then per-expert sums
+    __shared__ int s_table[kFusedTable];
+    const int n = a.n_blocks * L;
+    for (int i = threadIdx.x; i < n; i += kThreads) s_table[i] = a.ws_hist[i];
+    for (int b = threadIdx.x; b < a.n_blocks; b += kThreads) bad |= a.ws_bad[b] != 0;
+    __syncthreads();
+    for (int e = threadIdx.x; e < L; e += kThreads) {
+      int pre = 0, sum = 0;
+      for (int b = 0; b < a.n_blocks; ++b) {
+        const int v = s_table[b * L + e];
+        pre += b < blk ? v : 0;
+        sum += v;
+      }
+      s_base[e] = pre;
+      s_cnt[e] = sum;
+    }
+  }
+  if (bad) atomicOr(&s_flags, MOE_FLAG_BAD_EXPERT_ID);
+  __syncthreads();
+  // capacity: rows per expert are clipped at R
+  for (int e = threadIdx.x; e < L; e += kThreads) {
+    int c = s_cnt[e];
+    if (a.R > 0 && c > a.R) {
+      atomicOr(&s_flags, MOE_FLAG_CAPACITY);
+      atomicAdd(&s_dropped, c - a.R);
+      c = a.R;
+    }
+    s_cnt[e] = c;
+    s_off[e] = c;
+    s_tile[e] = (c + a.BM - 1) / a.BM;
+  }
+  __syncthreads();
+  if (a.R > 0) {
+    for (int e = threadIdx.x; e <= L; e += kThreads) s_off[e] = e * a.R;
+  } else {
+    const int total = block_exclusive_scan(s_off, L, s_part);
+    if (threadIdx.x == 0) s_off[L] = total;
+  }
+  const int tiles = block_exclusive_scan(s_tile, L, s_part);
+  if (threadIdx.x == 0) s_tile[L] = tiles;
+  __syncthreads();
+  if (blk == 0) {
+    for (int e = threadIdx.x; e <= L; e += kThreads) {
+      if (e < L) a.counts[e] = s_cnt[e];
+      a.offsets[e] = s_off[e];
+      a.tile_offsets[e] = s_tile[e];
+    }
+    if (threadIdx.x == 0) {
+      a.dev_status[0] = s_flags;
+      a.dev_status[1] = s_dropped;
+    }
+  }
+  if (blk < a.n_blocks) place_routes(a, blk, s_base, s_off);
+  fill_padding(a, blk, s_cnt, s_off);
 }
 
 }  // namespace
@@ -330,16 +461,25 @@ extern "C" moe_status moe_dispatch_layout(const int32_t* topk_ids, int T, int K,
   a.ws_hist = static_cast<int32_t*>(workspace);
   a.ws_bad = a.ws_hist + static_cast<int64_t>(a.n_blocks) * L;
 
-  if (a.n_blocks > 0) {
-    layout_count_kernel<<<a.n_blocks, kThreads, 0, stream>>>(a);
-    MOE_LAUNCH_CHECK();
-  }
-  layout_scan_kernel<<<1, kScanThreads, 0, stream>>>(a);
-  MOE_LAUNCH_CHECK();
   // at least enough blocks to sweep row_src's padding in a few passes
   const int64_t fill_blocks = (rows_cap + kThreads * 8 - 1) / (kThreads * 8);
   const int grid = static_cast<int>(std::max<int64_t>(std::max<int64_t>(a.n_blocks, fill_blocks), 1));
-  layout_place_kernel<<<grid, kThreads, 0, stream>>>(a);
+  if (a.n_blocks <= 1) {
+    // one block's share of routes: a single launch
+    layout_fused_kernel<true><<<grid, kThreads, 0, stream>>>(a);
+    MOE_LAUNCH_CHECK();
+    return MOE_OK;
+  }
+  layout_count_kernel<<<a.n_blocks, kThreads, 0, stream>>>(a);
+  MOE_LAUNCH_CHECK();
+  if (static_cast<int64_t>(a.n_blocks) * L <= kFusedTable) {
+    // every place block reads the whole histogram table itself
+    layout_fused_kernel<false><<<grid, kThreads, 0, stream>>>(a);
+  } else {
+    layout_scan_kernel<<<1, kScanThreads, 0, stream>>>(a);
+    MOE_LAUNCH_CHECK();
+    layout_place_kernel<<<grid, kThreads, 0, stream>>>(a);
+  }
   MOE_LAUNCH_CHECK();
   return MOE_OK;
 }

@@ -56,8 +56,12 @@ def test_layout_bit_exact(ep, name):
     check_layout(run_layout(ep, ids, cfg.E, cfg.expert_begin, cfg.L, cfg.R), ref)
 
 
+# The launch shape depends on T*K and L: one launch while T*K <= 1024
+# (all_invalid, overflow, single_*), two while ceil(T*K/1024) * L <= 16384,
+# three beyond (large_table).
 @pytest.mark.parametrize("case", ["empty", "all_invalid", "bad_ids", "overflow", "duplicates",
-                                  "many_experts", "exact_fit_random", "ragged", "bm64"])
+                                  "many_experts", "exact_fit_random", "ragged", "bm64",
+                                  "single_many_experts", "single_exact_fit", "large_table"])
 def test_layout_edge_cases(ep, case):
     announce("layout edge", case)
     rng = np.random.default_rng(3)
@@ -83,6 +87,15 @@ def test_layout_edge_cases(ep, case):
     elif case == "ragged":                        # T*K not a multiple of the block size
         E, e0, L, R = 32, 0, 32, 96
         ids = rng.integers(0, E, (1025, 3)).astype(np.int32)
+    elif case == "single_many_experts":           # one block, L > 64 ordered-chunk path
+        E, e0, L, R = 512, 100, 300, 6
+        ids = rng.integers(-1, E, (120, 8)).astype(np.int32)
+    elif case == "single_exact_fit":              # one block, offsets from the scan
+        E, e0, L, R = 64, 16, 32, 0
+        ids = rng.integers(-1, E, (150, 6)).astype(np.int32)
+    elif case == "large_table":                   # 20 blocks x 1024 experts: separate scan launch
+        E, e0, L, R = 2048, 512, 1024, 12
+        ids = rng.integers(-1, E, (4000, 5)).astype(np.int32)
     else:
         E, e0, L, R, BM = 16, 4, 8, 200, 64
         ids = rng.integers(-1, E, (999, 5)).astype(np.int32)
