@@ -106,19 +106,25 @@ def replay_consumer(prog):
 def replay_producer(prog):
     """-> (barriers, {stage: barrier count at the wait that landed all of
     its loads}, [(stage, barrier count at issue)])"""
+    from collections import Counter
     b, issued, landed, issues = 0, [], 0, []
+    n_issued, n_landed = Counter(), Counter()
     landed_at = {}
     for kind, a in prog:
         if kind == "bar":
             b += 1
         elif kind == "issue":
             issued.append(a)
+            n_issued[a] += 1
             issues.append((a, b))
         else:
-            landed = max(landed, len(issued) - a)
-            done = issued[:landed]
-            for s in set(done):
-                if s not in landed_at and issued.count(s) == done.count(s):
+            upto = max(landed, len(issued) - a)
+            newly = set(issued[landed:upto])
+            for s in issued[landed:upto]:
+                n_landed[s] += 1
+            landed = upto
+            for s in newly:                           # only these can have just completed
+                if s not in landed_at and n_landed[s] == n_issued[s]:
                     landed_at[s] = b
     return b, landed_at, issues
 
@@ -139,13 +145,16 @@ def check(K, tiles, fp8, fp8_epilogue, programs=None):
             for pk, (_, landed_at, _) in prod.items():
                 lb = landed_at.get(s)
                 assert lb is not None and lb < b, (K, ck, s, pk, lb, b)
+    last_read = {}                                    # (consumer, stage) -> barrier count of its read
+    for ck, (_, reads) in cons.items():
+        for s2, b2 in reads:
+            last_read[ck, s2] = max(b2, last_read.get((ck, s2), -1))
     for pk, (_, _, issues) in prod.items():
         for s, b in issues:
             if s >= NST:
-                for ck, (_, reads) in cons.items():
-                    for s2, b2 in reads:
-                        if s2 == s - NST:
-                            assert b2 < b, (K, pk, s, ck, b2, b)
+                for ck in cons:
+                    b2 = last_read.get((ck, s - NST))
+                    assert b2 is None or b2 < b, (K, pk, s, ck, b2, b)
 
 
 @pytest.mark.parametrize("fp8,fp8_epilogue", [(True, True), (True, False), (False, False)])
