@@ -80,16 +80,19 @@ __global__ __launch_bounds__(kThreads) void silu_mul_kernel(const float* __restr
 }
 
 constexpr int kMaxK = 64;
-constexpr int kCPL = 8;          // 8-column chunks per lane in flight per source row
+constexpr int kCPL = 4;                         // 8-column chunks per lane in one part
+constexpr int kPartChunks = kCPL * MOE_WAVE;    // 2048 columns per part
 
 template <bool kInBf16, bool kOutBf16>
 __global__ __launch_bounds__(kThreads) void combine_kernel(const uint8_t* __restrict__ eo,
                                                            const int32_t* __restrict__ slot_of,
                                                            const float* __restrict__ w, int T,
                                                            int K, int H, int64_t rows_cap,
-                                                           uint8_t* __restrict__ y) {
+                                                           uint8_t* __restrict__ y, int parts) {
   const int lane = moe::lane_id();
-  const int t = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+  const int item = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);   // (token, part)
+  const int t = item / parts;
+  const int p = item - t * parts;
   if (t >= T) return;
   constexpr int IB = kInBf16 ? 2 : 4;
   constexpr int OB = kOutBf16 ? 2 : 4;
@@ -98,68 +101,96 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const uint8_t* __rest
   // bit mask in k order (ballot bit k = lane k)
   const int s_l = lane < K ? slot_of[static_cast<int64_t>(t) * K + lane] : -1;
   const float w_l = lane < K ? w[static_cast<int64_t>(t) * K + lane] : 0.f;
-  const uint64_t routes = __ballot(s_l >= 0 && s_l < rows_cap);
+  uint64_t m = __ballot(s_l >= 0 && s_l < rows_cap);
   const int nchunk = H / 8;
-  uint8_t* yrow = y + static_cast<int64_t>(t) * H * OB;
-  for (int c0 = 0; c0 < nchunk; c0 += kCPL * MOE_WAVE) {
-    float acc[kCPL][8];
+  const int c0 = p * kPartChunks + lane;         // chunk u of this lane: c0 + 64u
+
+  float acc[kCPL][8];
 #pragma unroll
-    for (int u = 0; u < kCPL; ++u)
+  for (int u = 0; u < kCPL; ++u)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[u][i] = 0.f;
-    for (uint64_t m = routes; m; m &= m - 1) {
-      const int k = __builtin_ctzll(m);            // increasing k
-      const int s = __builtin_amdgcn_readlane(s_l, k);
-      const float wk = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w_l), k));
-      const uint4* row = reinterpret_cast<const uint4*>(eo + static_cast<int64_t>(s) * H * IB);
-      uint4 raw[kCPL][NV];
-#pragma unroll
-      for (int u = 0; u < kCPL; ++u) {
-        const int c = c0 + u * MOE_WAVE + lane;
-#pragma unroll
-        for (int v = 0; v < NV; ++v)
-          raw[u][v] = c < nchunk ? row[static_cast<int64_t>(c) * NV + v] : make_uint4(0, 0, 0, 0);
-      }
-#pragma unroll
-      for (int u = 0; u < kCPL; ++u) {
-        float v[8];
-        if constexpr (kInBf16) {
-          const uint32_t ww[4] = {raw[u][0].x, raw[u][0].y, raw[u][0].z, raw[u][0].w};
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            v[2 * i] = __uint_as_float(ww[i] << 16);
-            v[2 * i + 1] = __uint_as_float(ww[i] & 0xffff0000u);
-          }
-        } else {
-          const uint32_t ww[8] = {raw[u][0].x, raw[u][0].y, raw[u][0].z, raw[u][0].w,
-                                  raw[u][NV - 1].x, raw[u][NV - 1].y, raw[u][NV - 1].z, raw[u][NV - 1].w};
-#pragma unroll
-          for (int i = 0; i < 8; ++i) v[i] = __uint_as_float(ww[i]);
-        }
-        {
-          // product and sum rounded separately, in k order (no FMA contraction)
-#pragma clang fp contract(off)
-#pragma unroll
-          for (int i = 0; i < 8; ++i) acc[u][i] = acc[u][i] + wk * v[i];
-        }
-      }
-    }
+    for (int i = 0; i < 8; ++i) acc[u][i] = 0.f;
+  auto load = [&](int s, uint4 (*r)[NV]) {
+    const uint4* row = reinterpret_cast<const uint4*>(eo + static_cast<int64_t>(s) * H * IB);
 #pragma unroll
     for (int u = 0; u < kCPL; ++u) {
-      const int c = c0 + u * MOE_WAVE + lane;
-      if (c >= nchunk) break;
-      uint8_t* dst = yrow + static_cast<int64_t>(c) * 8 * OB;
-      if constexpr (kOutBf16) {
-        uint4 o;
-        o.x = moe::f32_to_bf16(acc[u][0]) | (uint32_t(moe::f32_to_bf16(acc[u][1])) << 16);
-        o.y = moe::f32_to_bf16(acc[u][2]) | (uint32_t(moe::f32_to_bf16(acc[u][3])) << 16);
-        o.z = moe::f32_to_bf16(acc[u][4]) | (uint32_t(moe::f32_to_bf16(acc[u][5])) << 16);
-        o.w = moe::f32_to_bf16(acc[u][6]) | (uint32_t(moe::f32_to_bf16(acc[u][7])) << 16);
-        moe::store_nt16(dst, o);
+      const int c = c0 + u * MOE_WAVE;
+#pragma unroll
+      for (int v = 0; v < NV; ++v)
+        r[u][v] = c < nchunk ? moe::load_nt16(row + static_cast<int64_t>(c) * NV + v) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto accumulate = [&](const uint4 (*r)[NV], float wk) {
+#pragma unroll
+    for (int u = 0; u < kCPL; ++u) {
+      float v[8];
+      if constexpr (kInBf16) {
+        const uint32_t ww[4] = {r[u][0].x, r[u][0].y, r[u][0].z, r[u][0].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          v[2 * i] = __uint_as_float(ww[i] << 16);
+          v[2 * i + 1] = __uint_as_float(ww[i] & 0xffff0000u);
+        }
       } else {
-        reinterpret_cast<float4*>(dst)[0] = make_float4(acc[u][0], acc[u][1], acc[u][2], acc[u][3]);
-        reinterpret_cast<float4*>(dst)[1] = make_float4(acc[u][4], acc[u][5], acc[u][6], acc[u][7]);
+        const uint32_t ww[8] = {r[u][0].x, r[u][0].y, r[u][0].z, r[u][0].w,
+                                r[u][NV - 1].x, r[u][NV - 1].y, r[u][NV - 1].z, r[u][NV - 1].w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = __uint_as_float(ww[i]);
       }
+      {
+        // product and sum rounded separately, in k order (no FMA contraction)
+#pragma clang fp contract(off)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[u][i] = acc[u][i] + wk * v[i];
+      }
+    }
+  };
+  auto route = [&](int k, int& s, float& wk) {
+    s = __builtin_amdgcn_readlane(s_l, k);
+    wk = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w_l), k));
+  };
+  // walk the local routes in increasing k; the next route's loads are issued
+  // before this route's sums
+  if (m) {
+    uint4 cur[kCPL][NV], nxt[kCPL][NV];
+    int s;
+    float wk;
+    route(__builtin_ctzll(m), s, wk);
+    load(s, cur);
+    for (;;) {
+      m &= m - 1;
+      const bool more = m != 0;
+      int s2 = 0;
+      float wk2 = 0.f;
+      if (more) {
+        route(__builtin_ctzll(m), s2, wk2);
+        load(s2, nxt);
+      }
+      accumulate(cur, wk);
+      if (!more) break;
+#pragma unroll
+      for (int u = 0; u < kCPL; ++u)
+#pragma unroll
+        for (int v = 0; v < NV; ++v) cur[u][v] = nxt[u][v];
+      wk = wk2;
+    }
+  }
+  uint8_t* yrow = y + static_cast<int64_t>(t) * H * OB;
+#pragma unroll
+  for (int u = 0; u < kCPL; ++u) {
+    const int c = c0 + u * MOE_WAVE;
+    if (c >= nchunk) break;
+    uint8_t* dst = yrow + static_cast<int64_t>(c) * 8 * OB;
+    if constexpr (kOutBf16) {
+      uint4 o;
+      o.x = moe::f32_to_bf16(acc[u][0]) | (uint32_t(moe::f32_to_bf16(acc[u][1])) << 16);
+      o.y = moe::f32_to_bf16(acc[u][2]) | (uint32_t(moe::f32_to_bf16(acc[u][3])) << 16);
+      o.z = moe::f32_to_bf16(acc[u][4]) | (uint32_t(moe::f32_to_bf16(acc[u][5])) << 16);
+      o.w = moe::f32_to_bf16(acc[u][6]) | (uint32_t(moe::f32_to_bf16(acc[u][7])) << 16);
+      moe::store_nt16(dst, o);
+    } else {
+      reinterpret_cast<float4*>(dst)[0] = make_float4(acc[u][0], acc[u][1], acc[u][2], acc[u][3]);
+      reinterpret_cast<float4*>(dst)[1] = make_float4(acc[u][4], acc[u][5], acc[u][6], acc[u][7]);
     }
   }
 }
@@ -197,18 +228,21 @@ extern "C" moe_status moe_combine(const void* expert_out, moe_dtype eo_dt, const
   MOE_CHECK(H % 8 == 0 && K <= kMaxK, MOE_ERR_UNSUPPORTED);
   if (T == 0) return MOE_OK;
   MOE_CHECK(slot_of && topk_weights && y && (rows_cap == 0 || expert_out), MOE_ERR_INVALID_ARG);
-  const int grid = (T + kRowsPerBlock - 1) / kRowsPerBlock;
+  const int parts = (H / 8 + kPartChunks - 1) / kPartChunks;
+  const int64_t grid64 = (static_cast<int64_t>(T) * parts + kRowsPerBlock - 1) / kRowsPerBlock;
+  MOE_CHECK(grid64 <= 0x7fffffff, MOE_ERR_UNSUPPORTED);
+  const int grid = static_cast<int>(grid64);
   auto* eo = static_cast<const uint8_t*>(expert_out);
   auto* yo = static_cast<uint8_t*>(y);
   const bool ib = eo_dt == MOE_BF16, ob = y_dt == MOE_BF16;
   if (ib && ob)
-    combine_kernel<true, true><<<grid, kThreads, 0, stream>>>(eo, slot_of, topk_weights, T, K, H, rows_cap, yo);
+    combine_kernel<true, true><<<grid, kThreads, 0, stream>>>(eo, slot_of, topk_weights, T, K, H, rows_cap, yo, parts);
   else if (ib)
-    combine_kernel<true, false><<<grid, kThreads, 0, stream>>>(eo, slot_of, topk_weights, T, K, H, rows_cap, yo);
+    combine_kernel<true, false><<<grid, kThreads, 0, stream>>>(eo, slot_of, topk_weights, T, K, H, rows_cap, yo, parts);
   else if (ob)
-    combine_kernel<false, true><<<grid, kThreads, 0, stream>>>(eo, slot_of, topk_weights, T, K, H, rows_cap, yo);
+    combine_kernel<false, true><<<grid, kThreads, 0, stream>>>(eo, slot_of, topk_weights, T, K, H, rows_cap, yo, parts);
   else
-    combine_kernel<false, false><<<grid, kThreads, 0, stream>>>(eo, slot_of, topk_weights, T, K, H, rows_cap, yo);
+    combine_kernel<false, false><<<grid, kThreads, 0, stream>>>(eo, slot_of, topk_weights, T, K, H, rows_cap, yo, parts);
   MOE_LAUNCH_CHECK();
   return MOE_OK;
 }

@@ -146,10 +146,24 @@ def run_permute(ep, cfg, x, ids):
     return layer
 
 
+def _permute_config(name):
+    """'<config>@<H>' is <config> with hidden size H: the permute kernels work on
+    1024-column (bf16 -> FP8) and 4 KB (copy) parts of a row, so H = 1152 and
+    2176 leave a ragged last part after one or two full ones."""
+    if "@" not in name:
+        return get_config(name)
+    base, h = name.split("@")
+    return get_config(base).scaled(name=name, H=int(h))
+
+
 @pytest.mark.parametrize("name", ["toy_fp32", "toy_bf16_fp8w", "decode_fp8", "prefill_fp8",
-                                  "skewed_bf16_small", "skewed_bf16", "prefill_fp8_small"])
+                                  "skewed_bf16_small", "skewed_bf16", "prefill_fp8_small",
+                                  "manyrow_bf16_small", "manyrow_fp8_small", "manyrow_fp32_small",
+                                  "prefill_fp8_small@1152", "prefill_fp8_small@2176",
+                                  "skewed_bf16_small@1152", "skewed_bf16_small@2176",
+                                  "toy_fp32@1152"])
 def test_permute_bit_exact(ep, name):
-    cfg = get_config(name)
+    cfg = _permute_config(name)
     announce("permute", name)
     ids, _ = make_routing(cfg)
     x = make_activations(cfg)
