@@ -14,11 +14,13 @@
 //   2. scan  : one block turns the histograms into exclusive prefixes over
 //              blocks (ws_hist in place), totals -> counts, offsets,
 //              tile_offsets, dev_status.
-//   3. place : every block re-reads its routes; inside each 64-route
-//              wavefront chunk the rank of a route among equal experts comes
-//              from ballot + mbcnt; chunk ranks are scanned in LDS and added
-//              to the block prefix.  Writes slot_of and row_src, and marks
-//              padding rows of row_src with -1.
+//   3. place : every block stages its 1024 routes in LDS; inside each
+//              64-route wavefront chunk a route ORs its lane bit into its
+//              expert's lane mask in LDS, and its rank among equal experts
+//              is the number of mask bits below it (L <= 64; larger L walks
+//              the chunks in order); chunk counts are scanned in LDS and
+//              added to the block prefix.  Writes
+//              slot_of and row_src, and marks padding rows of row_src -1.
 // Launches: one (count, scan and place fused) when the routes fit one
 // block's share; two (count, then scan fused into place: each block reads
 // the whole histogram table) while that table is small; otherwise three.
@@ -37,6 +39,7 @@ constexpr int kMaxL = 1024;
 // place block reads whole instead of a separate scan launch
 constexpr int64_t kFusedTable = 16384;
 
+
 struct LayoutArgs {
   const int32_t* ids;
   int64_t n_pairs;   // T*K
@@ -53,25 +56,42 @@ struct LayoutArgs {
   int32_t* ws_bad;     // [n_blocks]
 };
 
-// local expert of a route, -1 if none; *bad set for ids outside [-1, E)
-__device__ __forceinline__ int local_expert(const LayoutArgs& a, int64_t p, bool* bad) {
-  if (p >= a.n_pairs) return -1;
-  int g = a.ids[p];
+// local expert of route id g, -1 if none; *bad set for ids outside [-1, E)
+__device__ __forceinline__ int local_of(const LayoutArgs& a, int g, bool* bad) {
   if (g < -1 || g >= a.E_global) { *bad = true; return -1; }
-  int e = g - a.expert_begin;
+  const int e = g - a.expert_begin;
   return (g >= 0 && e >= 0 && e < a.L) ? e : -1;
+}
+
+// The four routes 4t..4t+3 of block blk's share (thread t); positions past
+// the last route read as -1 (no route).  One 16-byte load when the ids are
+// 16-byte aligned.
+__device__ __forceinline__ int4 load_route_ids(const LayoutArgs& a, int blk) {
+  const int64_t p = static_cast<int64_t>(blk) * kPairsPerBlock + 4 * threadIdx.x;
+  if ((reinterpret_cast<uintptr_t>(a.ids) & 15) == 0 && p + 4 <= a.n_pairs)
+    return *reinterpret_cast<const int4*>(a.ids + p);
+  int v[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) v[j] = p + j < a.n_pairs ? a.ids[p + j] : -1;
+  return make_int4(v[0], v[1], v[2], v[3]);
+}
+
+__device__ __forceinline__ void put_ids(int* s_ids, const int4& v) {
+  reinterpret_cast<int4*>(s_ids)[threadIdx.x] = v;
 }
 
 __global__ __launch_bounds__(kThreads) void layout_count_kernel(LayoutArgs a) {
   __shared__ int hist[kMaxL];
   __shared__ int any_bad;
+  const int4 v = load_route_ids(a, blockIdx.x);
   for (int e = threadIdx.x; e < a.L; e += kThreads) hist[e] = 0;
   if (threadIdx.x == 0) any_bad = 0;
   __syncthreads();
-  const int64_t base = static_cast<int64_t>(blockIdx.x) * kPairsPerBlock;
   bool bad = false;
-  for (int i = threadIdx.x; i < kPairsPerBlock; i += kThreads) {
-    int e = local_expert(a, base + i, &bad);
+  const int g[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = local_of(a, g[j], &bad);
     if (e >= 0) atomicAdd(&hist[e], 1);
   }
   if (bad) any_bad = 1;
@@ -167,40 +187,40 @@ __global__ __launch_bounds__(kScanThreads) void layout_scan_kernel(LayoutArgs a)
 }
 
 __shared__ int s_chunk_cnt[kChunksPerBlock][64];  // per chunk, per expert (L <= 64 path)
+__shared__ uint32_t s_lane_mask[kWaves][64][2];     // per wave, per expert: lanes of the chunk
 
-// Block blk's routes -> slot_of / row_src.  base[e]: routes of expert e in
-// earlier blocks; off[e]: first row of expert e.  Block-uniform call (it
+// Block blk's routes -> slot_of / row_src.  s_ids: the block's route ids in
+// LDS (put_ids, synchronised); base[e]: routes of expert e in earlier
+// blocks; off[e]: first row of expert e.  Block-uniform call (it
 // synchronises the block).
-__device__ void place_routes(const LayoutArgs& a, int blk, int* base, const int* off) {
+__device__ void place_routes(const LayoutArgs& a, int blk, const int* s_ids, int* base, const int* off) {
   const int L = a.L;
   const int wave = threadIdx.x / MOE_WAVE;
   const int lane = moe::lane_id();
   const int64_t pbase = static_cast<int64_t>(blk) * kPairsPerBlock;
 
-  // Per-chunk rank among equal experts.  For L <= 64 the per-chunk counts
-  // live in LDS and one scan over chunks follows; for larger L the block's
-  // chunks are processed in order with a running per-expert counter.
+  // Per-chunk rank among equal experts.  For L <= 64 every lane ORs its bit
+  // into its expert's 64-bit lane mask (LDS, one mask set per wave); the
+  // rank is the number of mask bits below the lane and the lowest lane
+  // records the chunk's count.  Per-chunk counts are then scanned over
+  // chunks.  For larger L the block's chunks are processed in order with a
+  // running per-expert counter.
   int e_of[kChunksPerBlock / kWaves];
   int rank[kChunksPerBlock / kWaves];
   if (L <= 64) {
-    for (int i = threadIdx.x; i < kChunksPerBlock * 64; i += kThreads)
-      (&s_chunk_cnt[0][0])[i] = 0;
-    __syncthreads();
     for (int r = 0; r < kChunksPerBlock / kWaves; ++r) {
       const int c = r * kWaves + wave;
       bool bad = false;
-      const int e = local_expert(a, pbase + c * MOE_WAVE + lane, &bad);
-      uint64_t left = moe::ballot(e >= 0);
+      const int e = local_of(a, s_ids[c * MOE_WAVE + lane], &bad);
+      s_lane_mask[wave][lane][0] = 0;             // LDS ops of one wave complete in order
+      s_lane_mask[wave][lane][1] = 0;
+      s_chunk_cnt[c][lane] = 0;
+      if (e >= 0) atomicOr(&s_lane_mask[wave][e][lane >> 5], 1u << (lane & 31));
       int my_rank = 0;
-      while (left) {
-        const int leader = __builtin_ctzll(left);
-        const int le = __builtin_amdgcn_readlane(e, leader);
-        const uint64_t m = moe::ballot(e == le);
-        if (e == le) {
-          my_rank = moe::mbcnt(m);
-          if (lane == leader) s_chunk_cnt[c][le] = __builtin_popcountll(m);
-        }
-        left &= ~m;
+      if (e >= 0) {
+        const uint64_t m = s_lane_mask[wave][e][0] | (static_cast<uint64_t>(s_lane_mask[wave][e][1]) << 32);
+        my_rank = moe::mbcnt(m);
+        if (my_rank == 0) s_chunk_cnt[c][e] = __builtin_popcountll(m);
       }
       e_of[r] = e;
       rank[r] = my_rank;
@@ -209,6 +229,7 @@ __device__ void place_routes(const LayoutArgs& a, int blk, int* base, const int*
     // exclusive scan over the block's chunks, per expert
     for (int e = threadIdx.x; e < L; e += kThreads) {
       int run = 0;
+#pragma unroll
       for (int c = 0; c < kChunksPerBlock; ++c) {
         int v = s_chunk_cnt[c][e];
         s_chunk_cnt[c][e] = run;
@@ -245,7 +266,7 @@ __device__ void place_routes(const LayoutArgs& a, int blk, int* base, const int*
       uint64_t mask_of_mine = 0;
       if (wave == 0) {
         bool bad = false;
-        e = local_expert(a, p, &bad);
+        e = local_of(a, s_ids[c * MOE_WAVE + lane], &bad);
         uint64_t left = moe::ballot(e >= 0);
         while (left) {
           const int leader = __builtin_ctzll(left);
@@ -275,55 +296,69 @@ __device__ void place_routes(const LayoutArgs& a, int blk, int* base, const int*
   }
 }
 
-// padding rows of row_src -> -1 (valid rows are written by place_routes)
+// padding rows of row_src -> -1 (valid rows are written by place_routes).
+// rows_cap < 2^31, so the expert of row q is a 32-bit quotient.
 __device__ void fill_padding(const LayoutArgs& a, int blk, const int* cnt, const int* off) {
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
-  for (int64_t q = static_cast<int64_t>(blk) * kThreads + threadIdx.x; q < a.rows_cap; q += stride) {
-    bool pad;
-    if (a.R > 0) {
-      const int e = static_cast<int>(q / a.R);
-      pad = (q - static_cast<int64_t>(e) * a.R) >= cnt[e];
-    } else {
-      pad = q >= off[a.L];
+  const uint32_t stride = gridDim.x * kThreads;
+  const uint32_t n = static_cast<uint32_t>(a.rows_cap);
+  if (a.R > 0) {
+    const uint32_t R = static_cast<uint32_t>(a.R);
+    for (uint32_t q = blk * kThreads + threadIdx.x; q < n; q += stride) {
+      const uint32_t e = q / R;
+      if (q - e * R >= static_cast<uint32_t>(cnt[e])) a.row_src[q] = -1;
     }
-    if (pad) a.row_src[q] = -1;
+  } else {
+    for (uint32_t q = static_cast<uint32_t>(off[a.L]) + blk * kThreads + threadIdx.x; q < n; q += stride)
+      a.row_src[q] = -1;
   }
 }
 
 __global__ __launch_bounds__(kThreads) void layout_place_kernel(LayoutArgs a) {
   __shared__ int base[kMaxL];
+  __shared__ __attribute__((aligned(16))) int s_ids[kPairsPerBlock];
   const int blk = blockIdx.x;
   if (blk < a.n_blocks) {
+    put_ids(s_ids, load_route_ids(a, blk));
     const int32_t* pre = a.ws_hist + static_cast<int64_t>(blk) * a.L;
     for (int e = threadIdx.x; e < a.L; e += kThreads) base[e] = pre[e];
-    place_routes(a, blk, base, a.offsets);
+    __syncthreads();
+    place_routes(a, blk, s_ids, base, a.offsets);
   }
   fill_padding(a, blk, a.counts, a.offsets);
 }
 
 // exclusive scan of v[0..n) in place by the block's threads (n <= kMaxL);
-// returns the total.  Block-uniform call.
+// returns the total.  Each thread sums a run of entries, the runs are
+// scanned inside each wave with shuffles and across the waves through
+// part[kWaves].  Block-uniform call.
 __device__ int block_exclusive_scan(int* v, int n, int* part) {
   const int t = threadIdx.x;
+  const int lane = moe::lane_id();
+  const int w = t / MOE_WAVE;
   const int per = (n + kThreads - 1) / kThreads;
   const int i0 = t * per;
   int s = 0;
   for (int i = i0; i < min(i0 + per, n); ++i) s += v[i];
-  part[t] = s;
+  int x = s;                                     // inclusive scan within the wave
+#pragma unroll
+  for (int d = 1; d < MOE_WAVE; d <<= 1) {
+    const int y = __shfl_up(x, d);
+    if (lane >= d) x += y;
+  }
+  if (lane == MOE_WAVE - 1) part[w] = x;
   __syncthreads();
-  for (int d = 1; d < kThreads; d <<= 1) {
-    const int x = t >= d ? part[t - d] : 0;
-    __syncthreads();
-    part[t] += x;
-    __syncthreads();
+  int before = 0, total = 0;
+#pragma unroll
+  for (int j = 0; j < kWaves; ++j) {
+    before += j < w ? part[j] : 0;
+    total += part[j];
   }
-  int run = part[t] - s;
+  int run = before + x - s;
   for (int i = i0; i < min(i0 + per, n); ++i) {
-    const int x = v[i];
+    const int y = v[i];
     v[i] = run;
-    run += x;
+    run += y;
   }
-  const int total = part[kThreads - 1];
   __syncthreads();
   return total;
 }
@@ -339,10 +374,15 @@ __global__ __launch_bounds__(kThreads) void layout_fused_kernel(LayoutArgs a) {
   __shared__ int s_cnt[kMaxL];
   __shared__ int s_off[kMaxL + 1];
   __shared__ int s_tile[kMaxL + 1];
-  __shared__ int s_part[kThreads];
+  __shared__ int s_part[kWaves];
+  __shared__ __attribute__((aligned(16))) int s_ids[kPairsPerBlock];
   __shared__ int s_flags, s_dropped;
   const int L = a.L;
   const int blk = blockIdx.x;
+  const bool placer = blk < a.n_blocks;
+  // Every global load this block needs is issued before its first use, so
+  // the launch pays few memory latencies instead of one per loop trip.
+  const int4 ids = load_route_ids(a, kSingle ? 0 : blk);
   for (int e = threadIdx.x; e < L; e += kThreads) {
     s_base[e] = 0;
     s_cnt[e] = 0;
@@ -351,29 +391,55 @@ __global__ __launch_bounds__(kThreads) void layout_fused_kernel(LayoutArgs a) {
     s_flags = 0;
     s_dropped = 0;
   }
-  __syncthreads();
   bool bad = false;
   if constexpr (kSingle) {
-    for (int64_t i = threadIdx.x; i < a.n_pairs; i += kThreads) {
-      const int e = local_expert(a, i, &bad);
+    // at most one block's share of routes (block 0's): every block
+    // histograms them itself, since the padding sweep of every block needs
+    // the counts; s_base stays 0
+    put_ids(s_ids, ids);
+    __syncthreads();
+    const int g[4] = {ids.x, ids.y, ids.z, ids.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = local_of(a, g[j], &bad);
       if (e >= 0) atomicAdd(&s_cnt[e], 1);
     }
   } else {
-    // the whole table through LDS: one coalesced sweep, then per-expert sums
+    // the count pass's per-block histograms, whole, through LDS
     __shared__ int s_table[kFusedTable];
+    constexpr int kBatch = 8;
     const int n = a.n_blocks * L;
-    for (int i = threadIdx.x; i < n; i += kThreads) s_table[i] = a.ws_hist[i];
+    for (int i0 = 0; i0 < n; i0 += kBatch * kThreads) {
+      int r[kBatch];
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        const int i = i0 + j * kThreads + threadIdx.x;
+        r[j] = i < n ? a.ws_hist[i] : 0;
+      }
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        const int i = i0 + j * kThreads + threadIdx.x;
+        if (i < n) s_table[i] = r[j];
+      }
+    }
     for (int b = threadIdx.x; b < a.n_blocks; b += kThreads) bad |= a.ws_bad[b] != 0;
+    put_ids(s_ids, ids);
     __syncthreads();
-    for (int e = threadIdx.x; e < L; e += kThreads) {
+    // per-expert totals and prefixes over blocks: thread t sums the blocks
+    // b = t / L (mod S) of expert t % L, S = max(1, threads / L) slices,
+    // and the slices meet in LDS atomics
+    const int S = L < kThreads ? kThreads / L : 1;
+    for (int t = threadIdx.x; t < L * S; t += kThreads) {
+      const int e = t % L;
       int pre = 0, sum = 0;
-      for (int b = 0; b < a.n_blocks; ++b) {
+#pragma unroll 4
+      for (int b = t / L; b < a.n_blocks; b += S) {
         const int v = s_table[b * L + e];
         pre += b < blk ? v : 0;
         sum += v;
       }
-      s_base[e] = pre;
-      s_cnt[e] = sum;
+      atomicAdd(&s_base[e], pre);
+      atomicAdd(&s_cnt[e], sum);
     }
   }
   if (bad) atomicOr(&s_flags, MOE_FLAG_BAD_EXPERT_ID);
@@ -411,7 +477,7 @@ __global__ __launch_bounds__(kThreads) void layout_fused_kernel(LayoutArgs a) {
       a.dev_status[1] = s_dropped;
     }
   }
-  if (blk < a.n_blocks) place_routes(a, blk, s_base, s_off);
+  if (placer) place_routes(a, blk, s_ids, s_base, s_off);
   fill_padding(a, blk, s_cnt, s_off);
 }
 

@@ -168,9 +168,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const uint8_t* __rest
       }
       accumulate(cur, wk);
       if (!more) break;
-#pragma unroll
       for (int u = 0; u < kCPL; ++u)
-#pragma unroll
         for (int v = 0; v < NV; ++v) cur[u][v] = nxt[u][v];
       wk = wk2;
     }
@@ -179,7 +177,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const uint8_t* __rest
 #pragma unroll
   for (int u = 0; u < kCPL; ++u) {
     const int c = c0 + u * MOE_WAVE;
-    if (c >= nchunk) break;
+    if (c >= nchunk) continue;
     uint8_t* dst = yrow + static_cast<int64_t>(c) * 8 * OB;
     if constexpr (kOutBf16) {
       uint4 o;
