@@ -19,6 +19,7 @@ __all__ = [
     "MoEError", "LIB_PATH", "lib", "MOE_F32", "MOE_BF16", "MOE_FP8_E4M3",
     "MOE_EPI_STORE_G", "MOE_EPI_SILU_MUL", "MOE_FLAG_CAPACITY", "MOE_FLAG_BAD_EXPERT_ID",
     "moe_status_string", "moe_abi_version", "moe_dispatch_layout_workspace_bytes",
+    "moe_grouped_gemm_workspace_bytes",
     "moe_dispatch_layout", "moe_permute", "moe_grouped_gemm_w13", "moe_silu_mul",
     "moe_grouped_gemm_w2", "moe_combine", "moe_router_topk", "dtype_code",
 ]
@@ -41,9 +42,12 @@ _SIG = {
     "moe_dispatch_layout_workspace_bytes": (_sz, [_i, _i, _i]),
     "moe_dispatch_layout": (_i, [_p, _i, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _sz, _p]),
     "moe_permute": (_i, [_p, _i, _i, _i, _i, _p, _i64, _p, _i, _p, _p]),
-    "moe_grouped_gemm_w13": (_i, [_p, _i, _p, _p, _i, _p, _p, _p, _i, _i64, _i, _i, _i, _p, _i, _p, _p]),
+    "moe_grouped_gemm_w13": (_i, [_p, _i, _p, _p, _i, _p, _p, _p, _i, _i64, _i, _i, _i, _p, _i, _p,
+                                  _p, _sz, _p]),
+    "moe_grouped_gemm_workspace_bytes": (_sz, []),
     "moe_silu_mul": (_i, [_p, _p, _p, _i, _i64, _i, _p, _i, _p, _p]),
-    "moe_grouped_gemm_w2": (_i, [_p, _i, _p, _p, _i, _p, _p, _p, _i, _i64, _i, _i, _p, _i, _p]),
+    "moe_grouped_gemm_w2": (_i, [_p, _i, _p, _p, _i, _p, _p, _p, _i, _i64, _i, _i, _p, _i, _p, _sz,
+                                 _p]),
     "moe_combine": (_i, [_p, _i, _p, _p, _i, _i, _i, _i64, _p, _i, _p]),
     "moe_router_topk": (_i, [_p, _p, _i, _i, _i, _i, _p, _p, _p]),
 }
@@ -71,6 +75,10 @@ def moe_abi_version() -> int:
 
 def moe_dispatch_layout_workspace_bytes(T: int, K: int, L: int) -> int:
     return int(lib.moe_dispatch_layout_workspace_bytes(T, K, L))
+
+
+def moe_grouped_gemm_workspace_bytes() -> int:
+    return int(lib.moe_grouped_gemm_workspace_bytes())
 
 
 # ---------------------------------------------------------------- marshalling helpers
@@ -140,15 +148,23 @@ def moe_permute(x, slot_of, buf, buf_scales=None) -> None:
         _ptr(buf, "buf"), dtype_code(buf), _f32(buf_scales, "buf_scales"), _stream(x)))
 
 
+def _ws(workspace):
+    if workspace is None:
+        return None, 0
+    return _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size()
+
+
 def moe_grouped_gemm_w13(a, a_scales, w13, w13_scales, counts, offsets, epi, out,
-                         out_scales=None) -> None:
-    """a [rows_cap,H], w13 [L,2I,H] -> G [rows_cap,2I] fp32 or Z [rows_cap,I]."""
+                         out_scales=None, workspace=None) -> None:
+    """a [rows_cap,H], w13 [L,2I,H] -> G [rows_cap,2I] fp32 or Z [rows_cap,I].
+    workspace: None, or a device buffer of moe_grouped_gemm_workspace_bytes()."""
     L, N, H = w13.shape
+    wp, wb = _ws(workspace)
     _check("moe_grouped_gemm_w13", lib.moe_grouped_gemm_w13(
         _ptr(a, "a"), dtype_code(a), _f32(a_scales, "a_scales"), _ptr(w13, "w13"),
         dtype_code(w13), _f32(w13_scales, "w13_scales"), _i32(counts, "counts"),
         _i32(offsets, "offsets"), L, a.shape[0], H, N // 2, int(epi), _ptr(out, "out"),
-        dtype_code(out), _f32(out_scales, "out_scales"), _stream(a)))
+        dtype_code(out), _f32(out_scales, "out_scales"), wp, wb, _stream(a)))
 
 
 def moe_silu_mul(g, counts, offsets, z, z_scales=None) -> None:
@@ -159,13 +175,15 @@ def moe_silu_mul(g, counts, offsets, z, z_scales=None) -> None:
         rows_cap, N // 2, _ptr(z, "z"), dtype_code(z), _f32(z_scales, "z_scales"), _stream(g)))
 
 
-def moe_grouped_gemm_w2(z, z_scales, w2, w2_scales, counts, offsets, out) -> None:
-    """z [rows_cap,I], w2 [L,H,I] -> out [rows_cap,H] (fp32|bf16)."""
+def moe_grouped_gemm_w2(z, z_scales, w2, w2_scales, counts, offsets, out, workspace=None) -> None:
+    """z [rows_cap,I], w2 [L,H,I] -> out [rows_cap,H] (fp32|bf16).
+    workspace: None, or a device buffer of moe_grouped_gemm_workspace_bytes()."""
     L, H, I = w2.shape
+    wp, wb = _ws(workspace)
     _check("moe_grouped_gemm_w2", lib.moe_grouped_gemm_w2(
         _ptr(z, "z"), dtype_code(z), _f32(z_scales, "z_scales"), _ptr(w2, "w2"), dtype_code(w2),
         _f32(w2_scales, "w2_scales"), _i32(counts, "counts"), _i32(offsets, "offsets"), L,
-        z.shape[0], H, I, _ptr(out, "out"), dtype_code(out), _stream(z)))
+        z.shape[0], H, I, _ptr(out, "out"), dtype_code(out), wp, wb, _stream(z)))
 
 
 def moe_combine(expert_out, slot_of, topk_weights, y) -> None:

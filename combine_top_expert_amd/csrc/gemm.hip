@@ -104,7 +104,17 @@ struct GemmArgs {
   void* out;
   float* out_scales;     // Z scales [rows_cap, I/128] (FP8 SiLU epilogue)
   int ldo;               // output row length in elements
+  float* part;           // K-split partial sums [grid][BM][2*BH] fp32, or null (no split)
+  int* desc;             // [grid][kDescInts]: the K-split piece each workgroup ran
 };
+
+constexpr int kDescInts = 16;
+constexpr int kPartFloats = BM * 2 * BH;           // one workgroup's partial tile
+constexpr int kMinPieces = 4;                      // K split only into >= 4 pieces
+// K split only for reductions of at least this many stages: the long gate/up
+// GEMMs, whose last round costs most; the host then launches the second
+// kernel, which costs a few microseconds even when no piece exists
+constexpr int kMinSplitStages = 32;
 
 // Rows of expert e that exist: counts[e] clipped to the buffer, so a tile
 // never reaches past rows_cap even for inconsistent counts/offsets.
@@ -197,12 +207,14 @@ __device__ __forceinline__ void decode_tile(int L, int nb_count, int t, int& e, 
   mt = local - nb * mte;
 }
 
-// One tile, workgroup-uniform.
+// One work item, workgroup-uniform: a tile, or one K-range piece of it.
 struct Tile {
   int e, nb, rows_valid, n0;
   int64_t row0;
   bool half1;
   int ws0, ws1;                        // FP8: first weight-scale index of each half
+  int ks0, nks;                        // K stages [ks0, ks0 + nks)
+  int split;                           // -1: whole tile; else the piece's index
 };
 
 // 32 bytes of one LDS row for an MFMA operand: 16-byte chunks at c0 and c1
@@ -249,22 +261,52 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs p) {
     __syncthreads();
   }
   const int n_tiles = s_mt_prefix[p.L] * p.nb_count;
-  int t_begin, t_end, t_step;
-  if (gridDim.x >= 8 && (gridDim.x & 7) == 0) {
-    const int xcd = blockIdx.x & 7;
-    const int per_xcd = gridDim.x >> 3;
-    t_begin = static_cast<int>((static_cast<int64_t>(n_tiles) * xcd) >> 3) + (blockIdx.x >> 3);
-    t_end = static_cast<int>((static_cast<int64_t>(n_tiles) * (xcd + 1)) >> 3);
-    t_step = per_xcd;
-  } else {
-    t_begin = blockIdx.x;
-    t_end = n_tiles;
-    t_step = gridDim.x;
-  }
-
   const int kstages = p.K * ESZ / KB;
   const int kgroups = p.K / 128;              // FP8 scale groups along K
   const int64_t lda = static_cast<int64_t>(p.K) * ESZ;
+  const bool stream = kstages >= 2;
+
+  // Work plan.  The workgroups form 8 XCD groups (workgroup i runs on XCD
+  // i mod 8); each group takes a contiguous chunk of the ordered tiles and
+  // walks it in whole rounds, slot j taking tiles j, j + slots, ...  When a
+  // workspace is bound (K of at least kMinSplitStages stages) and the
+  // chunk's last round would leave at least three quarters of its slots
+  // idle, each tile of that round is split along K into S = slots / tail
+  // pieces (at least two stages a piece); a piece leaves its fp32 sums in
+  // the workspace and a second kernel adds the pieces in order and applies
+  // the epilogue.  (With fewer idle slots the saved time does not cover the
+  // second launch and the partial traffic.)
+  int c_begin, c_len, slots, slot, bstride;
+  if (gridDim.x >= 8 && (gridDim.x & 7) == 0) {
+    const int xcd = blockIdx.x & 7;
+    slots = gridDim.x >> 3;
+    slot = blockIdx.x >> 3;
+    bstride = 8;
+    c_begin = static_cast<int>((static_cast<int64_t>(n_tiles) * xcd) >> 3);
+    c_len = static_cast<int>((static_cast<int64_t>(n_tiles) * (xcd + 1)) >> 3) - c_begin;
+  } else {
+    slots = gridDim.x;
+    slot = blockIdx.x;
+    bstride = 1;
+    c_begin = 0;
+    c_len = n_tiles;
+  }
+  const int full = c_len / slots;
+  const int tail = c_len - full * slots;
+  int S = 1;
+  if (p.part != nullptr && stream && tail > 0) {
+    S = min(slots / tail, kstages / 2);
+    if (S < kMinPieces) S = 1;
+  }
+  S = __builtin_amdgcn_readfirstlane(S);
+  const int my_full = full + ((S == 1 && slot < tail) ? 1 : 0);
+  const bool has_piece = S > 1 && slot < tail * S;
+  const int piece_tile = c_begin + full * slots + (has_piece ? slot / S : 0);
+  const int piece_split = has_piece ? slot % S : 0;
+  const int piece_ks0 = __builtin_amdgcn_readfirstlane(piece_split * kstages / S);
+  const int piece_nks = __builtin_amdgcn_readfirstlane((piece_split + 1) * kstages / S) - piece_ks0;
+  const int my_items = my_full + (has_piece ? 1 : 0);
+  const int total = my_full * kstages + (has_piece ? piece_nks : 0);
 
   auto make_tile = [&](int t) {
     Tile c;
@@ -281,20 +323,49 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs p) {
     const int bpe = p.N / 128;                 // weight-scale block rows per expert
     c.ws0 = (c.e * bpe + c.n0 / 128) * kgroups;
     c.ws1 = (c.e * bpe + (c.half1 ? c.n0 + p.half_stride : c.n0) / 128) * kgroups;
+    c.ks0 = 0;
+    c.nks = kstages;
+    c.split = -1;
     return c;
   };
+  // item ti of this workgroup: its whole tiles, then its piece
+  auto make_item = [&](int ti) {
+    if (ti < my_full) return make_tile(c_begin + slot + ti * slots);
+    Tile c = make_tile(piece_tile);
+    c.ks0 = piece_ks0;
+    c.nks = piece_nks;
+    c.split = piece_split;
+    return c;
+  };
+  // what the reduce kernel needs of this workgroup's piece
+  if (p.desc != nullptr && tid == 0) {
+    int* d = p.desc + static_cast<int64_t>(blockIdx.x) * kDescInts;
+    if (has_piece) {
+      const Tile c = make_tile(piece_tile);
+      d[0] = 1;
+      d[1] = S;
+      d[2] = piece_split;
+      d[3] = bstride;
+      d[4] = c.rows_valid;
+      d[5] = c.n0;
+      d[6] = c.nb;
+      d[7] = c.half1 ? 1 : 0;
+      d[8] = static_cast<int>(static_cast<uint32_t>(c.row0));
+      d[9] = static_cast<int>(c.row0 >> 32);
+    } else {
+      d[0] = 0;
+    }
+  }
 
-  // The workgroup's tiles form one stream of stages: stage g is K stage
-  // g % kstages of its (g / kstages)-th tile and lives in ring slot g % NST.
-  // With kstages >= 2, the first two stages of the next tile are staged
-  // during the last two stages of the current one, so a tile starts with its
-  // operands on the way instead of refilling the pipeline.
-  const int my_tiles = t_begin < t_end ? (t_end - t_begin + t_step - 1) / t_step : 0;
-  const int total = my_tiles * kstages;
-  const bool stream = kstages >= 2;
+  // The workgroup's items form one stream of stages: stage g lives in ring
+  // slot g % NST, and item ti's stages follow those of item ti - 1.  With
+  // kstages >= 2 (every item then has at least two stages), the first two
+  // stages of the next item are staged during the last two stages of the
+  // current one, so an item starts with its operands on the way instead of
+  // refilling the pipeline.
   Tile cur{}, nxt{};
-  if (my_tiles > 0) cur = make_tile(t_begin);
-  if (my_tiles > 1) nxt = make_tile(t_begin + t_step);
+  if (my_items > 0) cur = make_item(0);
+  if (my_items > 1) nxt = make_item(1);
 
   if (wave >= kConsumers) {
     // ================================================================ producers
@@ -370,12 +441,14 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs p) {
       }
     };
 
-    for (int ti = 0; ti < my_tiles; ++ti) {
-      const int base = ti * kstages;           // stream index of this tile's stage 0
-      auto staged = [&](int g) { return g < total && (stream || g < base + kstages); };
+    int base = 0;                              // stream index of the item's first stage
+    for (int ti = 0; ti < my_items; ++ti) {
+      const int nks = cur.nks;
+      auto staged = [&](int g) { return g < total && (stream || g < base + nks); };
       auto issue_g = [&](int g, int half) {
         const int ks = g - base;
-        if (ks < kstages) issue_half(cur, g % NST, ks, half); else issue_half(nxt, g % NST, ks - kstages, half);
+        if (ks < nks) issue_half(cur, g % NST, cur.ks0 + ks, half);
+        else issue_half(nxt, g % NST, nxt.ks0 + ks - nks, half);
       };
       if (ti == 0 || !stream) {
         __builtin_amdgcn_s_waitcnt(VmCnt<0>::imm);
@@ -391,7 +464,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs p) {
         }
         wg_barrier();                          // stage 0 has landed
       }
-      for (int ks = 0; ks < kstages; ++ks) {
+      for (int ks = 0; ks < nks; ++ks) {
         const int g = base + ks;
         const bool s2 = staged(g + 2);
         if (s2) issue_g(g + 2, 0);
@@ -404,10 +477,13 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs p) {
         }
         wg_barrier();
       }
-      wg_barrier();                            // the tile's last phase
-      if constexpr (EPI == EPI_SILU_FP8) wg_barrier();   // consumers' row-amax exchange
+      wg_barrier();                            // the item's last phase
+      if constexpr (EPI == EPI_SILU_FP8) {
+        if (cur.split < 0) wg_barrier();       // consumers' row-amax exchange
+      }
+      base += nks;
       cur = nxt;
-      if (ti + 2 < my_tiles) nxt = make_tile(t_begin + (ti + 2) * t_step);
+      if (ti + 2 < my_items) nxt = make_item(ti + 2);
     }
     return;
   }
@@ -425,8 +501,9 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs p) {
   const int s_frag = A_BYTES + B_BYTES + wm * 256 + frow * 16;
   const int w_frag = A_BYTES + B_BYTES + AS_BYTES;
 
-  for (int ti = 0; ti < my_tiles; ++ti) {
-    const int base = ti * kstages;
+  int base = 0;
+  for (int ti = 0; ti < my_items; ++ti) {
+    const int nks = cur.nks;
     const int nb = cur.nb, rows_valid = cur.rows_valid, n0 = cur.n0;
     const int64_t row0 = cur.row0;
     const bool half1 = cur.half1;
@@ -446,7 +523,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs p) {
     // Group g reads stage ks in phase 2*ks + g and multiplies it in phase
     // 2*ks + g + 1 (group 1 waits out phase 0, group 0 the last phase).
     if (wm == 1) wg_barrier();
-    for (int ks = 0; ks < kstages; ++ks) {
+    for (int ks = 0; ks < nks; ++ks) {
       const uint8_t* sb = s_ring + ((base + ks) % NST) * STAGE;
       v8i af[4], bf[2][2];
       i4 sa;
@@ -508,7 +585,20 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs p) {
     // 32*wn + 16*j + 4*(lane >> 4) + r of the half, r = 0..3.
     const int mrow = wm * 64 + frow;
     const int ncol = wn * 32 + 4 * (lane >> 4);
-    if constexpr (EPI == EPI_STORE_F32 || EPI == EPI_STORE_BF16) {
+    if (cur.split >= 0) {
+      // a K piece: its fp32 sums go to this workgroup's partial tile,
+      // row-major [BM][2*BH] (half h at columns h*BH + [0,BH))
+      float* pp = p.part + static_cast<int64_t>(blockIdx.x) * kPartFloats;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (mrow + 16 * i >= rows_valid) continue;
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            *reinterpret_cast<v4f*>(pp + (mrow + 16 * i) * (2 * BH) + h * BH + ncol + 16 * j) = acc[i][h][j];
+      }
+    } else if constexpr (EPI == EPI_STORE_F32 || EPI == EPI_STORE_BF16) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         if (h == 1 && !half1) continue;
@@ -594,20 +684,121 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs p) {
         }
       }
     }
+    base += nks;
     cur = nxt;
-    if (ti + 2 < my_tiles) nxt = make_tile(t_begin + (ti + 2) * t_step);
+    if (ti + 2 < my_items) nxt = make_item(ti + 2);
   }
+}
+
+// Second kernel of a K-split last round: workgroup b of the GEMM's grid
+// left a piece in partial tile b.  Blocks (b, y) of a tile's first piece add
+// the tile's S pieces in piece order (partial tiles b, b + bstride, ...) for
+// rows 8y .. 8y + 7 and apply the GEMM's epilogue to the valid ones.  A
+// half-wave of 32 lanes takes one row, 4 columns per lane per half.
+constexpr int kReduceThreads = 256;
+constexpr int kReduceRows = 2 * (kReduceThreads / MOE_WAVE);   // rows per block
+
+template <int EPI>
+__global__ __launch_bounds__(kReduceThreads) void gemm_piece_reduce_kernel(GemmArgs p) {
+  const int* d = p.desc + static_cast<int64_t>(blockIdx.x) * kDescInts;
+  if (d[0] == 0 || d[2] != 0) return;              // no piece, or not a tile's first one
+  const int S = d[1], bstride = d[3], rows_valid = d[4], n0 = d[5], nb = d[6];
+  const bool half1 = d[7] != 0;
+  const int64_t row0 = static_cast<int64_t>(static_cast<uint32_t>(d[8])) | (static_cast<int64_t>(d[9]) << 32);
+  const int lane = threadIdx.x & 63;
+  const int c4 = 4 * (lane & 31);
+  const int r = blockIdx.y * kReduceRows + 2 * (threadIdx.x / MOE_WAVE) + (lane >> 5);
+  if (r < rows_valid) {
+    v4f g[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const float* src = p.part + static_cast<int64_t>(blockIdx.x) * kPartFloats + r * (2 * BH) + h * BH + c4;
+      g[h] = *reinterpret_cast<const v4f*>(src);
+      for (int k = 1; k < S; ++k)
+        g[h] += *reinterpret_cast<const v4f*>(src + static_cast<int64_t>(k) * bstride * kPartFloats);
+    }
+    if constexpr (EPI == EPI_STORE_F32 || EPI == EPI_STORE_BF16) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        if (h == 1 && !half1) continue;
+        const int64_t o = (row0 + r) * p.ldo + n0 + h * p.half_stride + c4;
+        if constexpr (EPI == EPI_STORE_F32) {
+          *reinterpret_cast<v4f*>(static_cast<float*>(p.out) + o) = g[h];
+        } else {
+          *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + o) = make_uint2(
+              static_cast<uint32_t>(moe::f32_to_bf16(g[h][0])) | (static_cast<uint32_t>(moe::f32_to_bf16(g[h][1])) << 16),
+              static_cast<uint32_t>(moe::f32_to_bf16(g[h][2])) | (static_cast<uint32_t>(moe::f32_to_bf16(g[h][3])) << 16));
+        }
+      }
+    } else {
+      float z[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) z[k] = moe::silu(g[0][k]) * g[1][k];
+      const int64_t o = (row0 + r) * p.ldo + static_cast<int64_t>(nb) * BH + c4;
+      if constexpr (EPI == EPI_SILU_FP8) {
+        float m = fmaxf(fmaxf(fabsf(z[0]), fabsf(z[1])), fmaxf(fabsf(z[2]), fabsf(z[3])));
+        m = fmaxf(m, __shfl_xor(m, 1));
+        m = fmaxf(m, __shfl_xor(m, 2));
+        m = fmaxf(m, __shfl_xor(m, 4));
+        m = fmaxf(m, __shfl_xor(m, 8));
+        m = fmaxf(m, __shfl_xor(m, 16));
+        const float amax = moe::fp8_group_amax_clamp(m);
+        const float inv = moe::fp8_group_inv(amax);
+        *reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(p.out) + o) =
+            moe::f32x4_to_e4m3(z[0] * inv, z[1] * inv, z[2] * inv, z[3] * inv);
+        if ((lane & 31) == 0) p.out_scales[(row0 + r) * (p.ldo / 128) + nb] = moe::fp8_group_scale(amax);
+      } else if constexpr (EPI == EPI_SILU_F32) {
+        *reinterpret_cast<v4f*>(static_cast<float*>(p.out) + o) = v4f{z[0], z[1], z[2], z[3]};
+      } else {
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + o) = make_uint2(
+            static_cast<uint32_t>(moe::f32_to_bf16(z[0])) | (static_cast<uint32_t>(moe::f32_to_bf16(z[1])) << 16),
+            static_cast<uint32_t>(moe::f32_to_bf16(z[2])) | (static_cast<uint32_t>(moe::f32_to_bf16(z[3])) << 16));
+      }
+    }
+  }
+}
+
+int gemm_grid(int64_t max_tiles) {
+  int grid = static_cast<int>(std::min<int64_t>(max_tiles, moe_host::device_cu_count()));
+  if (grid >= 8) grid &= ~7;
+  return grid;
 }
 
 template <int DT, int EPI>
 moe_status launch(const GemmArgs& a, int max_mtiles, hipStream_t stream) {
   const int64_t max_tiles = static_cast<int64_t>(max_mtiles) * a.nb_count;
   if (max_tiles <= 0) return MOE_OK;
-  const int cus = moe_host::device_cu_count();
-  int grid = static_cast<int>(std::min<int64_t>(max_tiles, cus));
-  if (grid >= 8) grid &= ~7;
+  const int grid = gemm_grid(max_tiles);
   grouped_gemm_kernel<DT, EPI><<<grid, kThreads, 0, stream>>>(a);
   MOE_LAUNCH_CHECK();
+  if (a.part != nullptr) {
+    gemm_piece_reduce_kernel<EPI><<<dim3(grid, BM / kReduceRows), kReduceThreads, 0, stream>>>(a);
+    MOE_LAUNCH_CHECK();
+  }
+  return MOE_OK;
+}
+
+// workspace layout: partial tiles [grid][kPartFloats] fp32, then
+// descriptors [grid][kDescInts]
+size_t workspace_bytes_for_grid(int grid) {
+  return static_cast<size_t>(grid) * (kPartFloats * sizeof(float) + kDescInts * sizeof(int));
+}
+
+// Point the K-split at the caller's workspace; MOE_ERR_WORKSPACE if it is
+// given but too small for the launch's grid.
+moe_status bind_workspace(GemmArgs& g, int max_mtiles, int elem_bytes, void* ws, size_t ws_bytes) {
+  g.part = nullptr;
+  g.desc = nullptr;
+  if (ws == nullptr) return MOE_OK;
+  const int64_t max_tiles = static_cast<int64_t>(max_mtiles) * g.nb_count;
+  if (max_tiles <= 0) return MOE_OK;
+  const int grid = gemm_grid(max_tiles);
+  if (ws_bytes < workspace_bytes_for_grid(grid)) return MOE_ERR_WORKSPACE;
+  MOE_CHECK((reinterpret_cast<uintptr_t>(ws) & 15) == 0, MOE_ERR_INVALID_ARG);
+  // too few K stages for a split: no second launch
+  if (static_cast<int64_t>(g.K) * elem_bytes / KB < kMinSplitStages) return MOE_OK;
+  g.part = static_cast<float*>(ws);
+  g.desc = reinterpret_cast<int*>(static_cast<uint8_t*>(ws) + static_cast<size_t>(grid) * kPartFloats * sizeof(float));
   return MOE_OK;
 }
 
@@ -640,7 +831,7 @@ extern "C" moe_status moe_grouped_gemm_w13(const void* a, moe_dtype a_dt, const 
                                            const int32_t* counts, const int32_t* offsets, int L,
                                            int64_t rows_cap, int H, int I, moe_w13_epilogue epi,
                                            void* out, moe_dtype out_dt, float* out_scales,
-                                           hipStream_t stream) {
+                                           void* workspace, size_t workspace_bytes, hipStream_t stream) {
   MOE_CHECK(L >= 1 && L <= kMaxL && rows_cap >= 0 && H > 0 && I > 0, MOE_ERR_INVALID_ARG);
   MOE_CHECK(moe_host::valid_dtype(a_dt) && moe_host::valid_dtype(w_dt) && moe_host::valid_dtype(out_dt),
             MOE_ERR_INVALID_ARG);
@@ -673,6 +864,8 @@ extern "C" moe_status moe_grouped_gemm_w13(const void* a, moe_dtype a_dt, const 
   g.out = out;
   g.out_scales = out_scales;
   const int mt = max_row_tiles(rows_cap, L);
+  const moe_status ws_st = bind_workspace(g, mt, moe_host::elem_bytes(a_dt), workspace, workspace_bytes);
+  if (ws_st != MOE_OK) return ws_st;
   if (epi == MOE_EPI_STORE_G) {
     g.ldo = 2 * I;
     return dispatch_dt<EPI_STORE_F32>(a_dt, g, mt, stream);
@@ -689,7 +882,8 @@ extern "C" moe_status moe_grouped_gemm_w2(const void* z, moe_dtype z_dt, const f
                                           const void* w2, moe_dtype w_dt, const float* w2_scales,
                                           const int32_t* counts, const int32_t* offsets, int L,
                                           int64_t rows_cap, int H, int I, void* out,
-                                          moe_dtype out_dt, hipStream_t stream) {
+                                          moe_dtype out_dt, void* workspace, size_t workspace_bytes,
+                                          hipStream_t stream) {
   MOE_CHECK(L >= 1 && L <= kMaxL && rows_cap >= 0 && H > 0 && I > 0, MOE_ERR_INVALID_ARG);
   MOE_CHECK(moe_host::valid_dtype(z_dt) && moe_host::valid_dtype(w_dt) && moe_host::valid_dtype(out_dt),
             MOE_ERR_INVALID_ARG);
@@ -719,6 +913,12 @@ extern "C" moe_status moe_grouped_gemm_w2(const void* z, moe_dtype z_dt, const f
   g.out = out;
   g.ldo = H;
   const int mt = max_row_tiles(rows_cap, L);
+  const moe_status ws_st = bind_workspace(g, mt, moe_host::elem_bytes(z_dt), workspace, workspace_bytes);
+  if (ws_st != MOE_OK) return ws_st;
   if (out_dt == MOE_F32) return dispatch_dt<EPI_STORE_F32>(z_dt, g, mt, stream);
   return dispatch_dt<EPI_STORE_BF16>(z_dt, g, mt, stream);
+}
+
+extern "C" size_t moe_grouped_gemm_workspace_bytes(void) {
+  return workspace_bytes_for_grid(gemm_grid(int64_t(1) << 30));
 }

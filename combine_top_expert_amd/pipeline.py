@@ -18,6 +18,7 @@ import torch
 
 from . import (MOE_EPI_SILU_MUL, MOE_EPI_STORE_G, moe_combine, moe_dispatch_layout,
                moe_dispatch_layout_workspace_bytes, moe_grouped_gemm_w2, moe_grouped_gemm_w13,
+               moe_grouped_gemm_workspace_bytes,
                moe_permute, moe_silu_mul)
 
 _TORCH = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8}
@@ -69,6 +70,10 @@ class MoELayer:
         self.dev_status = torch.zeros(2, **i32)
         ws = moe_dispatch_layout_workspace_bytes(s.T, s.K, s.L)
         self.workspace = torch.zeros(max(ws, 4), dtype=torch.uint8, device=dev)
+        # K-split partial sums of the GEMMs' last round (both GEMMs run on one
+        # stream, one after the other, so they share it)
+        self.gemm_workspace = torch.empty(moe_grouped_gemm_workspace_bytes(), dtype=torch.uint8,
+                                          device=dev)
         self.buf = torch.empty(rc, s.H, dtype=_TORCH[s.buf_dt], device=dev)
         self.buf_scales = (torch.empty(rc, s.H // 128, dtype=torch.float32, device=dev)
                            if s.buf_dt == "fp8" else None)
@@ -96,10 +101,12 @@ class MoELayer:
     def gemm_w13(self):
         if self.fused:
             moe_grouped_gemm_w13(self.buf, self.buf_scales, self.w13, self.w13_scales, self.counts,
-                                 self.offsets, MOE_EPI_SILU_MUL, self.z, self.z_scales)
+                                 self.offsets, MOE_EPI_SILU_MUL, self.z, self.z_scales,
+                                 workspace=self.gemm_workspace)
         else:
             moe_grouped_gemm_w13(self.buf, self.buf_scales, self.w13, self.w13_scales, self.counts,
-                                 self.offsets, MOE_EPI_STORE_G, self.g)
+                                 self.offsets, MOE_EPI_STORE_G, self.g,
+                                 workspace=self.gemm_workspace)
 
     def silu_mul(self):
         if not self.fused:
@@ -107,7 +114,7 @@ class MoELayer:
 
     def gemm_w2(self):
         moe_grouped_gemm_w2(self.z, self.z_scales, self.w2, self.w2_scales, self.counts,
-                            self.offsets, self.out)
+                            self.offsets, self.out, workspace=self.gemm_workspace)
 
     def combine(self, topk_weights):
         moe_combine(self.out, self.slot_of, topk_weights, self.y)

@@ -70,7 +70,8 @@ typedef enum moe_w13_epilogue {
 /* Human-readable name of a moe_status value (static string). */
 const char* moe_status_string(int status);
 
-/* ABI version; bumped on any signature change or added entry point (2: moe_router_topk). */
+/* ABI version; bumped on any signature change or added entry point (2: moe_router_topk;
+ * 3: GEMM workspace for the K-split last round). */
 int moe_abi_version(void);
 
 /* Bytes of device workspace moe_dispatch_layout needs for (T, K, L). */
@@ -154,6 +155,14 @@ moe_status moe_permute(const void* x, moe_dtype x_dt, int T, int K, int H,
  *        §4.4 fusion of SiLU*up with the group quantisation); out_dt in
  *        {MOE_F32, MOE_BF16, MOE_FP8_E4M3}; for FP8, out_scales
  *        [rows_cap, I/128] fp32 get the same per-128 recipe as moe_permute.
+ *   workspace  NULL, or >= moe_grouped_gemm_workspace_bytes() bytes of device
+ *        memory, 16-byte aligned, owned by the caller and not shared with a
+ *        concurrent GEMM call.  With a workspace, tiles of an incomplete last
+ *        round of the persistent schedule are split along K. Their fp32
+ *        partial sums meet in the workspace, and a second kernel on the same
+ *        stream adds them in a fixed order. Without one, no tile is split.
+ *        Results differ only in fp32 summation order.  A workspace that is
+ *        given but too small returns MOE_ERR_WORKSPACE.
  * dtype pairs (a_dt = w_dt): F32, BF16, FP8_E4M3.  Limits: H % 128 == 0,
  * I % 128 == 0, L <= 1024.
  */
@@ -162,7 +171,12 @@ moe_status moe_grouped_gemm_w13(const void* a, moe_dtype a_dt, const float* a_sc
                                 const int32_t* counts, const int32_t* offsets, int L,
                                 int64_t rows_cap, int H, int I, moe_w13_epilogue epi,
                                 void* out, moe_dtype out_dt, float* out_scales,
-                                hipStream_t stream);
+                                void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Device workspace bytes that moe_grouped_gemm_w13 and moe_grouped_gemm_w2
+ * use at most on the current device (one fp32 128 x 256 partial tile and a
+ * 64-byte descriptor per compute unit).  Host-only; no device work. */
+size_t moe_grouped_gemm_workspace_bytes(void);
 
 /*
  * moe_silu_mul -- Z = SiLU(G[:, :I]) * G[:, I:] on valid rows only
@@ -187,13 +201,15 @@ moe_status moe_silu_mul(const float* g, const int32_t* counts, const int32_t* of
  *   z [rows_cap,I] z_dt;  z_scales [rows_cap,I/128] fp32 for FP8
  *   w2 [L,H,I] w_dt == z_dt;  w2_scales [L,H/128,I/128] fp32 for FP8
  *   out [rows_cap,H] out_dt in {MOE_F32, MOE_BF16}
+ *   workspace, workspace_bytes  as for moe_grouped_gemm_w13
  * Limits: H % 128 == 0, I % 128 == 0, L <= 1024.
  */
 moe_status moe_grouped_gemm_w2(const void* z, moe_dtype z_dt, const float* z_scales,
                                const void* w2, moe_dtype w_dt, const float* w2_scales,
                                const int32_t* counts, const int32_t* offsets, int L,
                                int64_t rows_cap, int H, int I,
-                               void* out, moe_dtype out_dt, hipStream_t stream);
+                               void* out, moe_dtype out_dt,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * moe_combine -- weighted gather-sum back to token order.

@@ -34,9 +34,10 @@ def lib():
 def test_header_declares_the_entry_points():
     fns = declared_functions()
     for name in ["moe_dispatch_layout", "moe_permute", "moe_grouped_gemm_w13", "moe_silu_mul",
-                 "moe_grouped_gemm_w2", "moe_combine", "moe_router_topk"]:
+                 "moe_grouped_gemm_w2", "moe_combine", "moe_router_topk",
+                 "moe_grouped_gemm_workspace_bytes"]:
         assert name in fns
-    assert len(fns) == 10
+    assert len(fns) == 11
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -55,7 +56,7 @@ def test_status_strings_and_version(lib):
     assert lib.moe_status_string(0) == b"MOE_OK"
     assert lib.moe_status_string(-2) == b"MOE_ERR_UNSUPPORTED"
     assert lib.moe_status_string(12345) == b"MOE_ERR_UNKNOWN"
-    assert lib.moe_abi_version() == 2
+    assert lib.moe_abi_version() == 3
 
 
 def test_workspace_bytes(lib):
@@ -115,11 +116,12 @@ def test_gemm_argument_errors(lib):
     w13.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
                     ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int64,
                     ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_int,
-                    ctypes.c_void_p, ctypes.c_void_p]
+                    ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
 
-    def call(a_dt=2, w_dt=2, H=256, I=128, epi=1, out_dt=2, L=2, scales=True):
+    def call(a_dt=2, w_dt=2, H=256, I=128, epi=1, out_dt=2, L=2, scales=True, ws=None, ws_bytes=0):
         s = P() if scales else None
-        return w13(P(), a_dt, s, P(), w_dt, s, P(), P(), L, 256, H, I, epi, P(), out_dt, s, None)
+        return w13(P(), a_dt, s, P(), w_dt, s, P(), P(), L, 256, H, I, epi, P(), out_dt, s, ws,
+                   ws_bytes, None)
 
     assert call(a_dt=1, w_dt=2) == UNSUPPORTED
     assert call(H=200) == UNSUPPORTED
@@ -128,13 +130,19 @@ def test_gemm_argument_errors(lib):
     assert call(epi=5) == INVALID
     assert call(L=0) == INVALID
     assert call(scales=False) == INVALID
+    assert call(ws=P(), ws_bytes=64) == WORKSPACE     # a workspace below the query's size
     w2 = lib.moe_grouped_gemm_w2
     w2.restype = ctypes.c_int
     w2.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
                    ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int64,
-                   ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
-    assert w2(P(), 1, None, P(), 1, None, P(), P(), 2, 256, 256, 128, P(), 2, None) == UNSUPPORTED
-    assert w2(P(), 0, None, P(), 1, None, P(), P(), 2, 256, 256, 128, P(), 1, None) == UNSUPPORTED
+                   ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
+                   ctypes.c_size_t, ctypes.c_void_p]
+    assert w2(P(), 1, None, P(), 1, None, P(), P(), 2, 256, 256, 128, P(), 2, None, 0, None) == UNSUPPORTED
+    assert w2(P(), 0, None, P(), 1, None, P(), P(), 2, 256, 256, 128, P(), 1, None, 0, None) == UNSUPPORTED
+    assert w2(P(), 1, None, P(), 1, None, P(), P(), 2, 256, 256, 128, P(), 1, P(), 64, None) == WORKSPACE
+    q = lib.moe_grouped_gemm_workspace_bytes
+    q.restype, q.argtypes = ctypes.c_size_t, []
+    assert q() >= 128 * 256 * 4 * 8                   # a partial tile per workgroup of a grid
 
 
 def test_combine_and_silu_argument_errors(lib):
@@ -159,7 +167,7 @@ def test_python_binding_loads_and_matches_header(lib):
     import combine_top_expert_amd as ep
     for name in declared_functions():
         assert callable(getattr(ep, name)), name
-    assert ep.moe_abi_version() == 2
+    assert ep.moe_abi_version() == 3
     assert ep.moe_status_string(-1) == "MOE_ERR_INVALID_ARG"
 
 

@@ -4,10 +4,10 @@ The kernel keeps three LDS stages in a ring.  Four producer waves only
 issue direct-to-LDS loads; eight consumer waves in two groups only read
 LDS fragments and multiply, alternating read and matrix phases one phase
 apart.  Every phase ends with a workgroup barrier taken by all twelve waves.
-A workgroup's tiles form one stream of stages.  In the two phases of stream
-stage G a producer issues its loads of stage G + 2 (first half, barrier,
-second half) and then waits (vmcnt) until its loads of stage G + 1 have
-landed.  Producer 0 issues one extra load per stage (the FP8 weight scales),
+A workgroup's work items (whole tiles, then possibly one K-split piece of a
+tile) form one stream of stages.  In the two phases of stream stage G a
+producer issues its loads of stage G + 2 (first half, barrier, second half)
+and then waits (vmcnt) until its loads of stage G + 1 have landed.  Producer 0 issues one extra load per stage (the FP8 weight scales),
 first.  This test replays that program order for every role, for 1, 2 and
 5 tiles of many stage counts, and checks the properties the kernel relies
 on:
@@ -24,50 +24,51 @@ import pytest
 NST = 3          # LDS ring depth
 
 
-def _stream(K, tiles):
-    total = tiles * K
+def _items(K, tiles, piece=0):
+    """A workgroup's work items: (stages, whole tile?).  `tiles` whole tiles of
+    K stages, then optionally one K-split piece of `piece` stages (pieces
+    store raw partial sums and skip the FP8 epilogue's row-amax barrier)."""
+    return [(K, True)] * tiles + ([(piece, False)] if piece else [])
+
+
+def consumer_program(group, K, tiles=1, fp8_epilogue=True, piece=0):
+    items = _items(K, tiles, piece)
     stream = K >= 2
-
-    def staged_fn(base):
-        return lambda g: g < total and (stream or g < base + K)
-    return stream, staged_fn
-
-
-def consumer_program(group, K, tiles=1, fp8_epilogue=True):
-    stream, _ = _stream(K, tiles)
-    ev = []
-    for ti in range(tiles):
-        base = ti * K
+    ev, base = [], 0
+    for ti, (nks, whole) in enumerate(items):
         if ti == 0 or not stream:
             ev += [("bar", None), ("bar", None)]      # producers fill stage 0
         if group == 1:
-            ev.append(("bar", None))                  # group 1 sits out the tile's phase 0
-        for ks in range(K):
+            ev.append(("bar", None))                  # group 1 sits out the item's phase 0
+        for ks in range(nks):
             ev.append(("read", base + ks))
             ev.append(("bar", None))                  # end of read phase (reads complete)
             ev.append(("bar", None))                  # end of matrix phase
         if group == 0:
             ev.append(("bar", None))                  # group 0 sits out the last phase
-        if fp8_epilogue:
+        if fp8_epilogue and whole:
             ev.append(("bar", None))                  # row-amax exchange of the FP8 Z epilogue
+        base += nks
     return ev
 
 
-def producer_program(K, tiles=1, fp8=True, first=False, fp8_epilogue=True):
+def producer_program(K, tiles=1, fp8=True, first=False, fp8_epilogue=True, piece=0):
     """One producer wave.  FP8: 7 + 6 loads per stage (+1 weight-scale load
     issued first by producer 0); otherwise 6 + 6."""
-    stream, staged_fn = _stream(K, tiles)
+    items = _items(K, tiles, piece)
+    stream = K >= 2
+    total = sum(n for n, _ in items)
     halves = (7, 6) if fp8 else (6, 6)
     nload = sum(halves)
-    ev = []
+    ev, base = [], 0
 
     def issue(g, half):
         n = halves[half] + (1 if (fp8 and first and half == 0) else 0)
         return [("issue", g)] * n
 
-    for ti in range(tiles):
-        base = ti * K
-        staged = staged_fn(base)
+    for ti, (nks, whole) in enumerate(items):
+        def staged(g):
+            return g < total and (stream or g < base + nks)
         if ti == 0 or not stream:
             ev += [("wait", 0), ("bar", None)]
             ev += issue(base, 0) + issue(base, 1)
@@ -76,7 +77,7 @@ def producer_program(K, tiles=1, fp8=True, first=False, fp8_epilogue=True):
             else:
                 ev.append(("wait", 0))
             ev.append(("bar", None))
-        for ks in range(K):
+        for ks in range(nks):
             g = base + ks
             s2 = staged(g + 2)
             if s2:
@@ -87,9 +88,10 @@ def producer_program(K, tiles=1, fp8=True, first=False, fp8_epilogue=True):
             elif staged(g + 1):
                 ev.append(("wait", 0))
             ev.append(("bar", None))
-        ev.append(("bar", None))                      # the tile's last phase
-        if fp8_epilogue:
+        ev.append(("bar", None))                      # the item's last phase
+        if fp8_epilogue and whole:
             ev.append(("bar", None))
+        base += nks
     return ev
 
 
@@ -129,12 +131,12 @@ def replay_producer(prog):
     return b, landed_at, issues
 
 
-def check(K, tiles, fp8, fp8_epilogue, programs=None):
+def check(K, tiles, fp8, fp8_epilogue, programs=None, piece=0):
     progs = programs or {
-        "c0": consumer_program(0, K, tiles, fp8_epilogue),
-        "c1": consumer_program(1, K, tiles, fp8_epilogue),
-        "p0": producer_program(K, tiles, fp8, True, fp8_epilogue),
-        "p1": producer_program(K, tiles, fp8, False, fp8_epilogue),
+        "c0": consumer_program(0, K, tiles, fp8_epilogue, piece),
+        "c1": consumer_program(1, K, tiles, fp8_epilogue, piece),
+        "p0": producer_program(K, tiles, fp8, True, fp8_epilogue, piece),
+        "p1": producer_program(K, tiles, fp8, False, fp8_epilogue, piece),
     }
     cons = {k: replay_consumer(v) for k, v in progs.items() if k[0] == "c"}
     prod = {k: replay_producer(v) for k, v in progs.items() if k[0] == "p"}
@@ -162,6 +164,17 @@ def check(K, tiles, fp8, fp8_epilogue, programs=None):
 @pytest.mark.parametrize("K", list(range(1, 40)) + [56, 64, 112, 128])
 def test_staging_protocol(K, tiles, fp8, fp8_epilogue):
     check(K, tiles, fp8, fp8_epilogue)
+
+
+@pytest.mark.parametrize("fp8,fp8_epilogue", [(True, True), (False, False)])
+@pytest.mark.parametrize("tiles", [0, 1, 3])
+@pytest.mark.parametrize("K", [2, 3, 4, 7, 16, 56, 112])
+def test_staging_protocol_with_k_piece(K, tiles, fp8, fp8_epilogue):
+    """Whole tiles followed by one K-split piece of the last round (every
+    piece length the kernel can choose: at least 2 stages, at most K)."""
+    for piece in sorted({2, 3, K // 2, K} - {0, 1}):
+        if piece <= K:
+            check(K, tiles, fp8, fp8_epilogue, piece=piece)
 
 
 def test_protocol_model_detects_a_missing_wait():

@@ -233,3 +233,101 @@ def test_combine_weighted_sum_fact(ep, gold):
     torch.cuda.synchronize()
     assert y[0, 0].item() == g["combined"]
     assert torch.all(y[1] == 0)         # no local route -> 0
+
+
+def k_split_plan(n_tiles, grid, kstages, min_pieces=4, min_stages=32):
+    """The kernel's work plan per XCD group of workgroups: (whole rounds,
+    tiles in the last round, pieces per last-round tile).  The last round is
+    split only for K of at least `min_stages` stages, and only into at least
+    `min_pieces` pieces of at least two stages."""
+    if grid >= 8 and grid % 8 == 0:
+        slots, chunks = grid // 8, [((n_tiles * x) >> 3, (n_tiles * (x + 1)) >> 3) for x in range(8)]
+    else:
+        slots, chunks = grid, [(0, n_tiles)]
+    plan = []
+    for b, e in chunks:
+        full, tail = divmod(e - b, slots)
+        S = min(slots // tail, kstages // 2) if tail and kstages >= min_stages else 1
+        plan.append((full, tail, S if S >= min_pieces else 1))
+    return plan
+
+
+def gemm_grid(rows_cap, L, nb_count):
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    mt = min(rows_cap // 128 + L, -(-rows_cap // 128) + L)
+    g = min(mt * nb_count, cus)
+    return g & ~7 if g >= 8 else g
+
+
+# shapes whose last GEMM round is split along K (asserted below): few tiles
+# against a large capacity-sized grid, at least 32 K stages; between them
+# every epilogue kind of both GEMMs runs split
+K_SPLIT_CASES = {
+    "fp8_w13": ("prefill_fp8_small", dict(T=128, H=4096, I=1024)),
+    "bf16_w13": ("skewed_bf16_small", dict(T=128, E=8, L=8, H=2048, I=512, R=512)),
+    "bf16_w2": ("skewed_bf16_small", dict(T=64, E=8, L=8, H=2048, I=2048, R=512)),
+    "f32": ("toy_fp32", dict(H=1024, I=1024)),
+}
+
+
+@pytest.mark.parametrize("case", sorted(K_SPLIT_CASES))
+def test_gemm_k_split_matches_unsplit(ep, case):
+    """With a workspace the GEMMs split an incomplete last round along K and
+    add the pieces in a second kernel.  Against the unsplit launch (no
+    workspace) only the fp32 summation order differs: fp32 results agree to
+    1e-6 relative L2, bf16 ones to a rounding step, and FP8 Z codes may move
+    by one step where z sits on a rounding boundary."""
+    base, kw = K_SPLIT_CASES[case]
+    cfg = get_config(base).scaled(name=f"ksplit_{case}", **kw)
+    announce("k-split", cfg.name)
+    wl = make_workload(cfg)
+    inp = oracle_stage_inputs(wl)
+    esz = {"fp8": 1, "bf16": 2, "f32": 4}[cfg.wdt]
+    mts = int(sum(-(-int(c) // 128) for c in inp["counts"]))
+    splits = {}
+    for g, K, nb in [("w13", cfg.H, cfg.I // 128), ("w2", cfg.I, -(-cfg.H // 256))]:
+        plan = k_split_plan(mts * nb, gemm_grid(cfg.rows_cap, cfg.L, nb), K * esz // 128)
+        splits[g] = max(S for _, _, S in plan)
+    assert max(splits.values()) > 1, f"{cfg.name}: no K split in this shape ({splits})"
+    layer = make_layer_with_buffer(wl, inp, fused=True)
+    g_buf = torch.empty(cfg.rows_cap, 2 * cfg.I, dtype=torch.float32, device="cuda")
+    rows = inp["rows"]
+    outs = {}
+    for use_ws in (False, True):
+        ws = layer.gemm_workspace if use_ws else None
+        g_buf.zero_()
+        ep.moe_grouped_gemm_w13(layer.buf, layer.buf_scales, layer.w13, layer.w13_scales,
+                                layer.counts, layer.offsets, ep.MOE_EPI_STORE_G, g_buf, workspace=ws)
+        layer.z.zero_()
+        ep.moe_grouped_gemm_w13(layer.buf, layer.buf_scales, layer.w13, layer.w13_scales,
+                                layer.counts, layer.offsets, ep.MOE_EPI_SILU_MUL, layer.z,
+                                layer.z_scales, workspace=ws)
+        torch.cuda.synchronize()
+        if cfg.z_dt == "fp8":
+            z_codes = host_bits(layer.z)
+            z_vals = F.dequant_fp8_groups(z_codes, layer.z_scales.cpu().numpy())
+        else:
+            z_codes = z_vals = host_vals(layer.z)
+        if not use_ws:
+            z_in = layer.z.clone()
+            zs_in = None if layer.z_scales is None else layer.z_scales.clone()
+        layer.out.zero_()
+        ep.moe_grouped_gemm_w2(z_in, zs_in, layer.w2, layer.w2_scales, layer.counts,
+                               layer.offsets, layer.out, workspace=ws)
+        torch.cuda.synchronize()
+        outs[use_ws] = (host_vals(g_buf)[rows], z_vals[rows], host_vals(layer.out)[rows], z_codes[rows])
+    (g0, z0, o0, c0), (g1, z1, o1, c1) = outs[False], outs[True]
+    eg, ez, eo = rel_l2(g1, g0), rel_l2(z1, z0), rel_l2(o1, o0)
+    print(f"[metric] {cfg.name} split {splits} rel_l2 G={eg:.2e} Z={ez:.2e} out={eo:.2e}", flush=True)
+    assert eg < 1e-6
+    assert eo < (1e-6 if cfg.out_dt == "f32" else 4e-3)
+    if cfg.z_dt == "fp8":
+        # a group's scale may differ in its last bit; codes differ only at
+        # rounding boundaries
+        assert ez < 1e-3 and np.mean(c1 != c0) < 0.02
+    else:
+        assert ez < (1e-6 if cfg.z_dt == "f32" else 4e-3)
+    # and the split result against the oracle, at the GEMM tests' bars
+    ref = oracle_mlp(wl, inp)
+    ref_g = np.stack([ref["G"][int(q)] for q in rows])
+    assert rel_l2(g1, ref_g) < GEMM_REL_L2[cfg.wdt]
