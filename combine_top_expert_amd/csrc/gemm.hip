@@ -607,18 +607,27 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs p) {
         for (int i = 0; i < 4; ++i) {
           const int row = mrow + 16 * i;
           if (row >= rows_valid) continue;
-          const int64_t o = (row0 + row) * p.ldo + ncol0 + ncol;
+          if constexpr (EPI == EPI_STORE_F32) {
+            const int64_t o = (row0 + row) * p.ldo + ncol0 + ncol;
 #pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            const v4f v = acc[i][h][j];
-            if constexpr (EPI == EPI_STORE_F32) {
-              *reinterpret_cast<v4f*>(static_cast<float*>(p.out) + o + 16 * j) = v;
-            } else {
-              const uint2 w = make_uint2(
-                  static_cast<uint32_t>(moe::f32_to_bf16(v[0])) | (static_cast<uint32_t>(moe::f32_to_bf16(v[1])) << 16),
-                  static_cast<uint32_t>(moe::f32_to_bf16(v[2])) | (static_cast<uint32_t>(moe::f32_to_bf16(v[3])) << 16));
-              *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + o + 16 * j) = w;
-            }
+            for (int j = 0; j < 2; ++j) *reinterpret_cast<v4f*>(static_cast<float*>(p.out) + o + 16 * j) = acc[i][h][j];
+          } else {
+            // lanes 16 apart (column groups q, q ^ 1) trade one 4-column
+            // block, so each lane stores 8 contiguous columns (16 bytes)
+            const bool odd = (lane >> 4) & 1;
+            const v4f give = odd ? acc[i][h][0] : acc[i][h][1];
+            v4f got;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) got[r] = __shfl_xor(give[r], 16);
+            const v4f lo = odd ? got : acc[i][h][0];
+            const v4f hi = odd ? acc[i][h][1] : got;
+            const int c0 = odd ? 16 + 4 * ((lane >> 4) - 1) : 4 * (lane >> 4);
+            const int64_t o = (row0 + row) * p.ldo + ncol0 + wn * 32 + c0;
+            *reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.out) + o) = make_uint4(
+                static_cast<uint32_t>(moe::f32_to_bf16(lo[0])) | (static_cast<uint32_t>(moe::f32_to_bf16(lo[1])) << 16),
+                static_cast<uint32_t>(moe::f32_to_bf16(lo[2])) | (static_cast<uint32_t>(moe::f32_to_bf16(lo[3])) << 16),
+                static_cast<uint32_t>(moe::f32_to_bf16(hi[0])) | (static_cast<uint32_t>(moe::f32_to_bf16(hi[1])) << 16),
+                static_cast<uint32_t>(moe::f32_to_bf16(hi[2])) | (static_cast<uint32_t>(moe::f32_to_bf16(hi[3])) << 16));
           }
         }
       }
