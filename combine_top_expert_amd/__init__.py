@@ -19,7 +19,7 @@ __all__ = [
     "MoEError", "LIB_PATH", "lib", "MOE_F32", "MOE_BF16", "MOE_FP8_E4M3",
     "MOE_EPI_STORE_G", "MOE_EPI_SILU_MUL", "MOE_FLAG_CAPACITY", "MOE_FLAG_BAD_EXPERT_ID",
     "moe_status_string", "moe_abi_version", "moe_dispatch_layout_workspace_bytes",
-    "moe_grouped_gemm_workspace_bytes",
+    "moe_grouped_gemm_workspace_bytes", "moe_pack_w13", "MOE_W_ROW_MAJOR", "MOE_W_PACKED",
     "moe_dispatch_layout", "moe_permute", "moe_grouped_gemm_w13", "moe_silu_mul",
     "moe_grouped_gemm_w2", "moe_combine", "moe_router_topk", "dtype_code",
 ]
@@ -28,6 +28,7 @@ LIB_PATH = Path(os.environ.get("MOE_EP_LIB", Path(__file__).resolve().parent / "
 
 MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
 MOE_EPI_STORE_G, MOE_EPI_SILU_MUL = 0, 1
+MOE_W_ROW_MAJOR, MOE_W_PACKED = 0, 1
 MOE_FLAG_CAPACITY, MOE_FLAG_BAD_EXPERT_ID = 1, 2
 
 if not LIB_PATH.exists():
@@ -42,8 +43,9 @@ _SIG = {
     "moe_dispatch_layout_workspace_bytes": (_sz, [_i, _i, _i]),
     "moe_dispatch_layout": (_i, [_p, _i, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _sz, _p]),
     "moe_permute": (_i, [_p, _i, _i, _i, _i, _p, _i64, _p, _i, _p, _p]),
-    "moe_grouped_gemm_w13": (_i, [_p, _i, _p, _p, _i, _p, _p, _p, _i, _i64, _i, _i, _i, _p, _i, _p,
-                                  _p, _sz, _p]),
+    "moe_grouped_gemm_w13": (_i, [_p, _i, _p, _p, _i, _p, _i, _p, _p, _i, _i64, _i, _i, _i, _p, _i,
+                                  _p, _p, _sz, _p]),
+    "moe_pack_w13": (_i, [_p, _i, _i, _i, _i, _p, _p]),
     "moe_grouped_gemm_workspace_bytes": (_sz, []),
     "moe_silu_mul": (_i, [_p, _p, _p, _i, _i64, _i, _p, _i, _p, _p]),
     "moe_grouped_gemm_w2": (_i, [_p, _i, _p, _p, _i, _p, _p, _p, _i, _i64, _i, _i, _p, _i, _p, _sz,
@@ -154,15 +156,26 @@ def _ws(workspace):
     return _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size()
 
 
+def moe_pack_w13(w13, w13_packed) -> None:
+    """w13 [L,2I,H] -> w13_packed (same shape and dtype, bytes in the GEMM's
+    staging order; see moe_ep.h)."""
+    L, N, H = w13.shape
+    if w13_packed.shape != w13.shape or w13_packed.dtype != w13.dtype:
+        raise ValueError("w13_packed must match w13 in shape and dtype")
+    _check("moe_pack_w13", lib.moe_pack_w13(
+        _ptr(w13, "w13"), dtype_code(w13), L, H, N // 2, _ptr(w13_packed, "w13_packed"), _stream(w13)))
+
+
 def moe_grouped_gemm_w13(a, a_scales, w13, w13_scales, counts, offsets, epi, out,
-                         out_scales=None, workspace=None) -> None:
+                         out_scales=None, workspace=None, w13_layout=MOE_W_ROW_MAJOR) -> None:
     """a [rows_cap,H], w13 [L,2I,H] -> G [rows_cap,2I] fp32 or Z [rows_cap,I].
-    workspace: None, or a device buffer of moe_grouped_gemm_workspace_bytes()."""
+    workspace: None, or a device buffer of moe_grouped_gemm_workspace_bytes().
+    w13_layout: MOE_W_PACKED when w13 was written by moe_pack_w13."""
     L, N, H = w13.shape
     wp, wb = _ws(workspace)
     _check("moe_grouped_gemm_w13", lib.moe_grouped_gemm_w13(
         _ptr(a, "a"), dtype_code(a), _f32(a_scales, "a_scales"), _ptr(w13, "w13"),
-        dtype_code(w13), _f32(w13_scales, "w13_scales"), _i32(counts, "counts"),
+        dtype_code(w13), _f32(w13_scales, "w13_scales"), int(w13_layout), _i32(counts, "counts"),
         _i32(offsets, "offsets"), L, a.shape[0], H, N // 2, int(epi), _ptr(out, "out"),
         dtype_code(out), _f32(out_scales, "out_scales"), wp, wb, _stream(a)))
 

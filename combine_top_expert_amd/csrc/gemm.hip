@@ -106,6 +106,7 @@ struct GemmArgs {
   int ldo;               // output row length in elements
   float* part;           // K-split partial sums [grid][BM][2*BH] fp32, or null (no split)
   int* desc;             // [grid][kDescInts]: the K-split piece each workgroup ran
+  int w_packed;          // W in the packed layout (moe_pack_w13), else [L, N, K]
 };
 
 constexpr int kDescInts = 16;
@@ -384,6 +385,11 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs p) {
     const int srow = lane >> 3;
     const int voff_e = static_cast<int>(srow * lda) + (((lane & 7) ^ srow) << 4);
     const int voff_o = static_cast<int>(srow * lda) + (((lane & 7) ^ srow ^ 1) << 4);
+    // packed W: rows of one tile stage are 128 bytes apart
+    const int pvoff_e = srow * KB + (((lane & 7) ^ srow) << 4);
+    const int pvoff_o = srow * KB + (((lane & 7) ^ srow ^ 1) << 4);
+    const int64_t w_expert_bytes = p.w_packed ? static_cast<int64_t>(p.nb_count) * kstages * (2 * BH) * KB
+                                              : p.N * lda;
     const int spos = 32 * (pw & 1) + (lane & 31);
     const int soff = (64 * (pw >> 1) + 16 * (spos & 3) + (spos >> 2)) * kgroups * 4;
     // Buffer resources: A over the whole expert-major buffer, W over one
@@ -404,8 +410,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs p) {
     // ring slot s (FP8: 7 + 6 loads, plus the weight scales on producer 0)
     auto issue_half = [&](const Tile& c, int s, int ks, int half) {
       const __amdgpu_buffer_rsrc_t rW = __builtin_amdgcn_make_buffer_rsrc(
-          const_cast<uint8_t*>(p.W + static_cast<int64_t>(c.e) * p.N * lda), 0,
-          static_cast<int>(p.N * lda), kRsrcWord3);
+          const_cast<uint8_t*>(p.W + static_cast<int64_t>(c.e) * w_expert_bytes), 0,
+          static_cast<int>(w_expert_bytes), kRsrcWord3);
       uint8_t* st = s_ring + s * STAGE;
       if constexpr (kFp8) {
         if (half == 0 && pw == 0 && lane < 2)
@@ -425,14 +431,25 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs p) {
                                                  (j & 1) ? voff_o : voff_e,
                                                  a_off + static_cast<int>(8 * j * lda), 0, 0);
       }
-      const int w_off =
-          static_cast<int>((c.n0 + (pw >> 1) * (c.half1 ? p.half_stride : 0) + 64 * (pw & 1)) * lda) + ks * KB;
+      if (p.w_packed) {
+        // tile stage (nb, ks) of the expert: 2*BH rows x 128 bytes, contiguous
+        const int w_off = ((c.nb * kstages + ks) * (2 * BH) + 64 * pw) * KB;
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int j = 4 * half + jj;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rW, (lds_void)(st + A_BYTES + (64 * pw + 8 * j) * KB), 16,
-                                                 (j & 1) ? voff_o : voff_e,
-                                                 w_off + static_cast<int>(8 * j * lda), 0, 0);
+        for (int jj = 0; jj < 4; ++jj) {
+          const int j = 4 * half + jj;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rW, (lds_void)(st + A_BYTES + (64 * pw + 8 * j) * KB), 16,
+                                                   (j & 1) ? pvoff_o : pvoff_e, w_off + 8 * j * KB, 0, 0);
+        }
+      } else {
+        const int w_off =
+            static_cast<int>((c.n0 + (pw >> 1) * (c.half1 ? p.half_stride : 0) + 64 * (pw & 1)) * lda) + ks * KB;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int j = 4 * half + jj;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rW, (lds_void)(st + A_BYTES + (64 * pw + 8 * j) * KB), 16,
+                                                   (j & 1) ? voff_o : voff_e,
+                                                   w_off + static_cast<int>(8 * j * lda), 0, 0);
+        }
       }
       if constexpr (kFp8) {
         if (half == 0 && lane < 32)
@@ -767,6 +784,31 @@ __global__ __launch_bounds__(kReduceThreads) void gemm_piece_reduce_kernel(GemmA
   }
 }
 
+// W13 [L, 2I, H] -> packed [L][I/128][H*esz/128][2*BH rows][KB bytes]: tile
+// stage (nb, ks) holds gate rows nb*128 + [0,128) then up rows
+// I + nb*128 + [0,128), bytes [ks*128, ks*128 + 128) of each, so the
+// gate/up GEMM stages it with 1 KB contiguous loads.  One thread per
+// 16-byte chunk.
+__global__ __launch_bounds__(256) void pack_w13_kernel(const uint8_t* __restrict__ w, int64_t n_chunks, int I,
+                                                      int row_bytes, uint8_t* __restrict__ out) {
+  const int ks_count = row_bytes / KB;
+  const int nb_count = I / BH;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n_chunks;
+       i += static_cast<int64_t>(gridDim.x) * 256) {
+    const int c16 = static_cast<int>(i & 7);
+    int64_t q = i >> 3;
+    const int r = static_cast<int>(q % (2 * BH));
+    q /= 2 * BH;
+    const int ks = static_cast<int>(q % ks_count);
+    q /= ks_count;
+    const int nb = static_cast<int>(q % nb_count);
+    const int64_t e = q / nb_count;
+    const int64_t wrow = (r < BH ? 0 : I) + static_cast<int64_t>(nb) * BH + (r & (BH - 1));
+    const uint4 v = *reinterpret_cast<const uint4*>(w + (e * 2 * I + wrow) * row_bytes + ks * KB + c16 * 16);
+    *reinterpret_cast<uint4*>(out + i * 16) = v;
+  }
+}
+
 int gemm_grid(int64_t max_tiles) {
   int grid = static_cast<int>(std::min<int64_t>(max_tiles, moe_host::device_cu_count()));
   if (grid >= 8) grid &= ~7;
@@ -835,8 +877,25 @@ bool offsets_fit(int64_t K_bytes, int64_t N, int64_t rows_cap) {
 
 }  // namespace
 
+extern "C" moe_status moe_pack_w13(const void* w13, moe_dtype w_dt, int L, int H, int I, void* w13_packed,
+                                   hipStream_t stream) {
+  MOE_CHECK(L >= 1 && H > 0 && I > 0 && moe_host::valid_dtype(w_dt), MOE_ERR_INVALID_ARG);
+  MOE_CHECK(H % 128 == 0 && I % 128 == 0, MOE_ERR_UNSUPPORTED);
+  MOE_CHECK(w13 && w13_packed && w13 != w13_packed, MOE_ERR_INVALID_ARG);
+  MOE_CHECK(((reinterpret_cast<uintptr_t>(w13) | reinterpret_cast<uintptr_t>(w13_packed)) & 15) == 0,
+            MOE_ERR_INVALID_ARG);
+  const int row_bytes = H * moe_host::elem_bytes(w_dt);
+  const int64_t n_chunks = static_cast<int64_t>(L) * 2 * I * row_bytes / 16;
+  const int grid = static_cast<int>(std::min<int64_t>((n_chunks + 255) / 256, 65536));
+  pack_w13_kernel<<<grid, 256, 0, stream>>>(static_cast<const uint8_t*>(w13), n_chunks, I, row_bytes,
+                                           static_cast<uint8_t*>(w13_packed));
+  MOE_LAUNCH_CHECK();
+  return MOE_OK;
+}
+
 extern "C" moe_status moe_grouped_gemm_w13(const void* a, moe_dtype a_dt, const float* a_scales,
                                            const void* w13, moe_dtype w_dt, const float* w13_scales,
+                                           moe_weight_layout w13_layout,
                                            const int32_t* counts, const int32_t* offsets, int L,
                                            int64_t rows_cap, int H, int I, moe_w13_epilogue epi,
                                            void* out, moe_dtype out_dt, float* out_scales,
@@ -845,6 +904,7 @@ extern "C" moe_status moe_grouped_gemm_w13(const void* a, moe_dtype a_dt, const 
   MOE_CHECK(moe_host::valid_dtype(a_dt) && moe_host::valid_dtype(w_dt) && moe_host::valid_dtype(out_dt),
             MOE_ERR_INVALID_ARG);
   MOE_CHECK(epi == MOE_EPI_STORE_G || epi == MOE_EPI_SILU_MUL, MOE_ERR_INVALID_ARG);
+  MOE_CHECK(w13_layout == MOE_W_ROW_MAJOR || w13_layout == MOE_W_PACKED, MOE_ERR_INVALID_ARG);
   MOE_CHECK(a_dt == w_dt, MOE_ERR_UNSUPPORTED);
   MOE_CHECK(H % 128 == 0 && I % 128 == 0, MOE_ERR_UNSUPPORTED);
   MOE_CHECK(epi == MOE_EPI_SILU_MUL || out_dt == MOE_F32, MOE_ERR_UNSUPPORTED);
@@ -872,6 +932,7 @@ extern "C" moe_status moe_grouped_gemm_w13(const void* a, moe_dtype a_dt, const 
   g.rows_cap = rows_cap;
   g.out = out;
   g.out_scales = out_scales;
+  g.w_packed = w13_layout == MOE_W_PACKED;
   const int mt = max_row_tiles(rows_cap, L);
   const moe_status ws_st = bind_workspace(g, mt, moe_host::elem_bytes(a_dt), workspace, workspace_bytes);
   if (ws_st != MOE_OK) return ws_st;

@@ -18,7 +18,7 @@ import torch
 
 from . import (MOE_EPI_SILU_MUL, MOE_EPI_STORE_G, moe_combine, moe_dispatch_layout,
                moe_dispatch_layout_workspace_bytes, moe_grouped_gemm_w2, moe_grouped_gemm_w13,
-               moe_grouped_gemm_workspace_bytes,
+               moe_grouped_gemm_workspace_bytes, moe_pack_w13, MOE_W_PACKED, MOE_W_ROW_MAJOR,
                moe_permute, moe_silu_mul)
 
 _TORCH = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8}
@@ -83,10 +83,17 @@ class MoELayer:
                          if s.z_dt == "fp8" else None)
         self.out = torch.empty(rc, s.H, dtype=_TORCH[s.out_dt], device=dev)
         self.y = torch.empty(s.T, s.H, dtype=_TORCH[s.out_dt], device=dev)
-        self.w13 = self.w13_scales = self.w2 = self.w2_scales = None
+        self.w13 = self.w13_scales = self.w2 = self.w2_scales = self.w13_packed = None
 
-    def set_weights(self, w13, w2, w13_scales=None, w2_scales=None):
+    def set_weights(self, w13, w2, w13_scales=None, w2_scales=None, pack_w13=True):
+        """Device weights in the pages' layouts.  With pack_w13 (the default)
+        the gate/up weights are also packed once into the GEMM's staging
+        order (moe_pack_w13), which the gate/up GEMM then reads."""
         self.w13, self.w2, self.w13_scales, self.w2_scales = w13, w2, w13_scales, w2_scales
+        self.w13_packed = None
+        if pack_w13:
+            self.w13_packed = torch.empty_like(w13)
+            moe_pack_w13(w13, self.w13_packed)
 
     # ---- the six steps
     def layout(self, topk_ids):
@@ -99,14 +106,16 @@ class MoELayer:
         moe_permute(x, self.slot_of, self.buf, self.buf_scales)
 
     def gemm_w13(self):
+        w, lay = ((self.w13_packed, MOE_W_PACKED) if self.w13_packed is not None
+                  else (self.w13, MOE_W_ROW_MAJOR))
         if self.fused:
-            moe_grouped_gemm_w13(self.buf, self.buf_scales, self.w13, self.w13_scales, self.counts,
+            moe_grouped_gemm_w13(self.buf, self.buf_scales, w, self.w13_scales, self.counts,
                                  self.offsets, MOE_EPI_SILU_MUL, self.z, self.z_scales,
-                                 workspace=self.gemm_workspace)
+                                 workspace=self.gemm_workspace, w13_layout=lay)
         else:
-            moe_grouped_gemm_w13(self.buf, self.buf_scales, self.w13, self.w13_scales, self.counts,
+            moe_grouped_gemm_w13(self.buf, self.buf_scales, w, self.w13_scales, self.counts,
                                  self.offsets, MOE_EPI_STORE_G, self.g,
-                                 workspace=self.gemm_workspace)
+                                 workspace=self.gemm_workspace, w13_layout=lay)
 
     def silu_mul(self):
         if not self.fused:

@@ -63,6 +63,12 @@ typedef enum moe_w13_epilogue {
   MOE_EPI_SILU_MUL = 1        /* out = Z = SiLU(G[:, :I]) * G[:, I:]       */
 } moe_w13_epilogue;
 
+/* Layout of the gate/up weights given to moe_grouped_gemm_w13. */
+typedef enum moe_weight_layout {
+  MOE_W_ROW_MAJOR = 0,        /* [L, 2I, H]: [expert, out, in]                     */
+  MOE_W_PACKED = 1            /* as written by moe_pack_w13                        */
+} moe_weight_layout;
+
 /* Bits of dev_status[0] written by moe_dispatch_layout. */
 #define MOE_FLAG_CAPACITY 1      /* a local expert received more than R routes */
 #define MOE_FLAG_BAD_EXPERT_ID 2 /* an id was < -1 or >= E_global              */
@@ -71,7 +77,7 @@ typedef enum moe_w13_epilogue {
 const char* moe_status_string(int status);
 
 /* ABI version; bumped on any signature change or added entry point (2: moe_router_topk;
- * 3: GEMM workspace for the K-split last round). */
+ * 3: GEMM workspace for the K-split last round; 4: moe_pack_w13 and the W13 layout). */
 int moe_abi_version(void);
 
 /* Bytes of device workspace moe_dispatch_layout needs for (T, K, L). */
@@ -134,6 +140,22 @@ moe_status moe_permute(const void* x, moe_dtype x_dt, int T, int K, int H,
                        void* buf, moe_dtype buf_dt, float* buf_scales, hipStream_t stream);
 
 /*
+ * moe_pack_w13 -- the gate/up weights in the GEMM's staging order.
+ *
+ * Same bytes as w13 [L, 2I, H] (w_dt), rearranged so that each (128-column
+ * block nb of Z, 128-byte K stage ks) of an expert is one contiguous 32 KB
+ * run: [L][I/128][H*esz/128][256 rows][128 bytes], rows 0..127 the gate
+ * rows nb*128 + r, rows 128..255 the up rows I + nb*128 + r.  Values are
+ * copied, never converted; the FP8 block scales keep their layout.  The
+ * gate/up GEMM stages that layout with 1 KB contiguous loads instead of
+ * eight 128-byte row pieces.  Weights are static, so the caller packs once
+ * and keeps the packed copy (same size as w13, caller-owned,
+ * non-overlapping).  Limits: H % 128 == 0, I % 128 == 0.
+ */
+moe_status moe_pack_w13(const void* w13, moe_dtype w_dt, int L, int H, int I, void* w13_packed,
+                        hipStream_t stream);
+
+/*
  * moe_grouped_gemm_w13 -- gate/up projection of every local expert.
  *
  * For each expert e and valid row q of e: G[q, n] = sum_k A[q,k] W13[e,n,k]
@@ -147,6 +169,8 @@ moe_status moe_permute(const void* x, moe_dtype x_dt, int T, int K, int H,
  *
  *   a          [rows_cap,H]  a_dt;  a_scales [rows_cap,H/128] fp32 for FP8
  *   w13        [L,2I,H]      w_dt == a_dt; rows [0,I) are gate, [I,2I) up
+ *              (w13_layout MOE_W_ROW_MAJOR), or as packed by moe_pack_w13
+ *              (MOE_W_PACKED)
  *   w13_scales [L,2I/128,H/128] fp32 for FP8, else unused
  *   counts, offsets  [L], [L+1] as produced by moe_dispatch_layout
  *   epi == MOE_EPI_STORE_G:  out = G [rows_cap,2I], out_dt = MOE_F32
@@ -168,6 +192,7 @@ moe_status moe_permute(const void* x, moe_dtype x_dt, int T, int K, int H,
  */
 moe_status moe_grouped_gemm_w13(const void* a, moe_dtype a_dt, const float* a_scales,
                                 const void* w13, moe_dtype w_dt, const float* w13_scales,
+                                moe_weight_layout w13_layout,
                                 const int32_t* counts, const int32_t* offsets, int L,
                                 int64_t rows_cap, int H, int I, moe_w13_epilogue epi,
                                 void* out, moe_dtype out_dt, float* out_scales,

@@ -35,9 +35,9 @@ def test_header_declares_the_entry_points():
     fns = declared_functions()
     for name in ["moe_dispatch_layout", "moe_permute", "moe_grouped_gemm_w13", "moe_silu_mul",
                  "moe_grouped_gemm_w2", "moe_combine", "moe_router_topk",
-                 "moe_grouped_gemm_workspace_bytes"]:
+                 "moe_grouped_gemm_workspace_bytes", "moe_pack_w13"]:
         assert name in fns
-    assert len(fns) == 11
+    assert len(fns) == 12
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -56,7 +56,7 @@ def test_status_strings_and_version(lib):
     assert lib.moe_status_string(0) == b"MOE_OK"
     assert lib.moe_status_string(-2) == b"MOE_ERR_UNSUPPORTED"
     assert lib.moe_status_string(12345) == b"MOE_ERR_UNKNOWN"
-    assert lib.moe_abi_version() == 3
+    assert lib.moe_abi_version() == 4
 
 
 def test_workspace_bytes(lib):
@@ -114,13 +114,14 @@ def test_gemm_argument_errors(lib):
     w13 = lib.moe_grouped_gemm_w13
     w13.restype = ctypes.c_int
     w13.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
-                    ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int64,
-                    ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_int,
-                    ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+                    ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+                    ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                    ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
 
-    def call(a_dt=2, w_dt=2, H=256, I=128, epi=1, out_dt=2, L=2, scales=True, ws=None, ws_bytes=0):
+    def call(a_dt=2, w_dt=2, H=256, I=128, epi=1, out_dt=2, L=2, scales=True, ws=None, ws_bytes=0,
+             layout=0):
         s = P() if scales else None
-        return w13(P(), a_dt, s, P(), w_dt, s, P(), P(), L, 256, H, I, epi, P(), out_dt, s, ws,
+        return w13(P(), a_dt, s, P(), w_dt, s, layout, P(), P(), L, 256, H, I, epi, P(), out_dt, s, ws,
                    ws_bytes, None)
 
     assert call(a_dt=1, w_dt=2) == UNSUPPORTED
@@ -131,6 +132,15 @@ def test_gemm_argument_errors(lib):
     assert call(L=0) == INVALID
     assert call(scales=False) == INVALID
     assert call(ws=P(), ws_bytes=64) == WORKSPACE     # a workspace below the query's size
+    assert call(layout=2) == INVALID                  # unknown weight layout
+    pk = lib.moe_pack_w13
+    pk.restype = ctypes.c_int
+    pk.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                   ctypes.c_void_p, ctypes.c_void_p]
+    assert pk(P(16), 2, 2, 200, 128, P(4096), None) == UNSUPPORTED   # H % 128
+    assert pk(P(16), 2, 2, 256, 128, P(16), None) == INVALID         # in place
+    assert pk(P(16), 2, 2, 256, 128, P(4104), None) == INVALID       # misaligned output
+    assert pk(P(16), 2, 0, 256, 128, P(4096), None) == INVALID       # L = 0
     w2 = lib.moe_grouped_gemm_w2
     w2.restype = ctypes.c_int
     w2.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
@@ -167,7 +177,7 @@ def test_python_binding_loads_and_matches_header(lib):
     import combine_top_expert_amd as ep
     for name in declared_functions():
         assert callable(getattr(ep, name)), name
-    assert ep.moe_abi_version() == 3
+    assert ep.moe_abi_version() == 4
     assert ep.moe_status_string(-1) == "MOE_ERR_INVALID_ARG"
 
 

@@ -331,3 +331,43 @@ def test_gemm_k_split_matches_unsplit(ep, case):
     ref = oracle_mlp(wl, inp)
     ref_g = np.stack([ref["G"][int(q)] for q in rows])
     assert rel_l2(g1, ref_g) < GEMM_REL_L2[cfg.wdt]
+
+
+@pytest.mark.parametrize("name", ["toy_fp32", "toy_bf16_fp8w", "decode_fp8_small", "prefill_fp8_small",
+                                  "skewed_bf16_small", "manyrow_fp8_small"])
+def test_pack_w13_and_packed_gemm(ep, name):
+    """moe_pack_w13 writes the row-major weights' bytes in the staging order
+    [L][I/128][H*esz/128][gate 128 rows, up 128 rows][128 bytes], and the
+    gate/up GEMM gives bit-identical G and Z from either layout (same loads
+    into the same LDS positions, only the global addresses differ)."""
+    announce("pack w13", name)
+    wl = make_workload(name)
+    cfg = wl.cfg
+    inp = oracle_stage_inputs(wl)
+    layer = make_layer_with_buffer(wl, inp, fused=True)
+    L, H, I = cfg.L, cfg.H, cfg.I
+    rb = layer.w13.view(torch.uint8).cpu().numpy().reshape(L, 2 * I, -1)
+    ks = rb.shape[2] // 128
+    want = rb.reshape(L, 2, I // 128, 128, ks, 128).transpose(0, 2, 4, 1, 3, 5).ravel()
+    got = layer.w13_packed.view(torch.uint8).cpu().numpy().ravel()
+    assert np.array_equal(got, want)
+    g = torch.empty(cfg.rows_cap, 2 * I, dtype=torch.float32, device="cuda")
+    res = {}
+    for lay, w in [(ep.MOE_W_ROW_MAJOR, layer.w13), (ep.MOE_W_PACKED, layer.w13_packed)]:
+        g.fill_(float("nan"))
+        ep.moe_grouped_gemm_w13(layer.buf, layer.buf_scales, w, layer.w13_scales, layer.counts,
+                                layer.offsets, ep.MOE_EPI_STORE_G, g, w13_layout=lay,
+                                workspace=layer.gemm_workspace)
+        layer.z.zero_()
+        ep.moe_grouped_gemm_w13(layer.buf, layer.buf_scales, w, layer.w13_scales, layer.counts,
+                                layer.offsets, ep.MOE_EPI_SILU_MUL, layer.z, layer.z_scales,
+                                w13_layout=lay, workspace=layer.gemm_workspace)
+        torch.cuda.synchronize()
+        zs = None if layer.z_scales is None else layer.z_scales.cpu().numpy().copy()
+        res[lay] = (host_bits(g), host_bits(layer.z), zs)
+    rows = inp["rows"]
+    (g0, z0, s0), (g1, z1, s1) = res[ep.MOE_W_ROW_MAJOR], res[ep.MOE_W_PACKED]
+    assert np.array_equal(g0[rows].view(np.uint32), g1[rows].view(np.uint32))
+    assert np.array_equal(z0[rows], z1[rows])
+    if s0 is not None:
+        assert np.array_equal(s0[rows].view(np.uint32), s1[rows].view(np.uint32))
