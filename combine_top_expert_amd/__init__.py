@@ -20,6 +20,7 @@ __all__ = [
     "MOE_EPI_STORE_G", "MOE_EPI_SILU_MUL", "MOE_FLAG_CAPACITY", "MOE_FLAG_BAD_EXPERT_ID",
     "moe_status_string", "moe_abi_version", "moe_dispatch_layout_workspace_bytes",
     "moe_grouped_gemm_workspace_bytes", "moe_pack_w13", "MOE_W_ROW_MAJOR", "MOE_W_PACKED",
+    "moe_combine_backward", "moe_silu_mul_backward", "moe_permute_backward", "moe_transpose_weights",
     "moe_dispatch_layout", "moe_permute", "moe_grouped_gemm_w13", "moe_silu_mul",
     "moe_grouped_gemm_w2", "moe_combine", "moe_router_topk", "dtype_code",
 ]
@@ -52,6 +53,10 @@ _SIG = {
                                  _p]),
     "moe_combine": (_i, [_p, _i, _p, _p, _i, _i, _i, _i64, _p, _i, _p]),
     "moe_router_topk": (_i, [_p, _p, _i, _i, _i, _i, _p, _p, _p]),
+    "moe_combine_backward": (_i, [_p, _i, _p, _i, _p, _p, _i, _i, _i, _i64, _p, _i, _p, _p]),
+    "moe_silu_mul_backward": (_i, [_p, _p, _i, _p, _p, _i, _i64, _i, _p, _i, _p]),
+    "moe_permute_backward": (_i, [_p, _i, _p, _i, _i, _i, _i64, _p, _i, _p]),
+    "moe_transpose_weights": (_i, [_p, _i, _i, _i, _i, _p, _p]),
 }
 for _name, (_res, _args) in _SIG.items():
     if not hasattr(lib, _name):
@@ -215,3 +220,41 @@ def moe_router_topk(logits, K, topk_ids, topk_weights, bias=None, bias_in_weight
     _check("moe_router_topk", lib.moe_router_topk(
         _f32(logits, "logits"), _f32(bias, "bias"), T, E, K, 1 if bias_in_weights else 0,
         _i32(topk_ids, "topk_ids"), _f32(topk_weights, "topk_weights"), _stream(logits)))
+
+
+# ---------------------------------------------------------------- backward
+
+def moe_combine_backward(dy, expert_out, slot_of, topk_weights, d_out, d_weights) -> None:
+    """dy [T,H], expert_out [rows_cap,H] -> d_out [rows_cap,H] (local rows),
+    d_weights [T,K] fp32."""
+    T, K = slot_of.shape
+    _check("moe_combine_backward", lib.moe_combine_backward(
+        _ptr(dy, "dy"), dtype_code(dy), _ptr(expert_out, "expert_out"), dtype_code(expert_out),
+        _i32(slot_of, "slot_of"), _f32(topk_weights, "topk_weights"), T, K, dy.shape[1],
+        expert_out.shape[0], _ptr(d_out, "d_out"), dtype_code(d_out), _f32(d_weights, "d_weights"),
+        _stream(dy)))
+
+
+def moe_silu_mul_backward(g, dz, counts, offsets, dg) -> None:
+    """g [rows_cap,2I] fp32 (forward G), dz [rows_cap,I] -> dg [rows_cap,2I]."""
+    rows_cap, N = g.shape
+    _check("moe_silu_mul_backward", lib.moe_silu_mul_backward(
+        _f32(g, "g"), _ptr(dz, "dz"), dtype_code(dz), _i32(counts, "counts"), _i32(offsets, "offsets"),
+        counts.shape[0], rows_cap, N // 2, _ptr(dg, "dg"), dtype_code(dg), _stream(g)))
+
+
+def moe_permute_backward(d_buf, slot_of, dx) -> None:
+    """d_buf [rows_cap,H] -> dx [T,H] = sum over each token's local rows."""
+    T, K = slot_of.shape
+    _check("moe_permute_backward", lib.moe_permute_backward(
+        _ptr(d_buf, "d_buf"), dtype_code(d_buf), _i32(slot_of, "slot_of"), T, K, dx.shape[1],
+        d_buf.shape[0], _ptr(dx, "dx"), dtype_code(dx), _stream(dx)))
+
+
+def moe_transpose_weights(w, wt) -> None:
+    """w [L,N,K] -> wt [L,K,N]."""
+    L, N, K = w.shape
+    if tuple(wt.shape) != (L, K, N) or wt.dtype != w.dtype:
+        raise ValueError("wt must be [L,K,N] of w's dtype")
+    _check("moe_transpose_weights", lib.moe_transpose_weights(
+        _ptr(w, "w"), dtype_code(w), L, N, K, _ptr(wt, "wt"), _stream(w)))

@@ -1,0 +1,264 @@
+// Backward of the MoE path: combine backward, SiLU*up backward and the weight
+// transpose that lets the grouped GEMM compute both data gradients.
+//
+// ("XTuner Domino EP": the DeepEP part's complete run path, whose backward
+// consumes the saved routing in reverse order, and the UltraEP part's
+// backward sketch -- combine backward, the grouped GEMMs' gradients, inverse
+// permutation.  The formulas are the derivatives of the forward definition
+// of "SGLang、NCCL 与 MoE EP" §1.1 and "SGLang Expert Compute Backend" §1.1,
+// §3.6.)
+//
+//   d_out[q]  = w[t,k] * dy[t]                 combine backward (a dispatch)
+//   d_w[t,k]  = <dy[t], out[q]>                router-weight gradient
+//   dZ        = d_out W2[e]     = d_out (W2[e]^T)^T    grouped GEMM, W2 transposed
+//   dG        = SiLU*up backward of (G, dZ)
+//   dA        = dG W13[e]      = dG (W13[e]^T)^T       grouped GEMM, W13 transposed
+//   dx[t]     = sum_k dA[q(t,k)]               permute backward (unit-weight combine)
+
+#include <algorithm>
+
+#include "moe_common.h"
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWavesPerBlock = kThreads / MOE_WAVE;
+
+template <bool kF32>
+__device__ __forceinline__ void load8(const uint8_t* row, int c, float* v) {
+  // 8 values starting at column 8c
+  if constexpr (kF32) {
+    const uint4 a = reinterpret_cast<const uint4*>(row)[2 * c];
+    const uint4 b = reinterpret_cast<const uint4*>(row)[2 * c + 1];
+    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = __uint_as_float(w[i]);
+  } else {
+    const uint4 a = reinterpret_cast<const uint4*>(row)[c];
+    const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+}
+
+template <bool kF32>
+__device__ __forceinline__ void store8(uint8_t* row, int c, const float* v) {
+  if constexpr (kF32) {
+    reinterpret_cast<float4*>(row)[2 * c] = make_float4(v[0], v[1], v[2], v[3]);
+    reinterpret_cast<float4*>(row)[2 * c + 1] = make_float4(v[4], v[5], v[6], v[7]);
+  } else {
+    uint4 o;
+    o.x = moe::f32_to_bf16(v[0]) | (uint32_t(moe::f32_to_bf16(v[1])) << 16);
+    o.y = moe::f32_to_bf16(v[2]) | (uint32_t(moe::f32_to_bf16(v[3])) << 16);
+    o.z = moe::f32_to_bf16(v[4]) | (uint32_t(moe::f32_to_bf16(v[5])) << 16);
+    o.w = moe::f32_to_bf16(v[6]) | (uint32_t(moe::f32_to_bf16(v[7])) << 16);
+    reinterpret_cast<uint4*>(row)[c] = o;
+  }
+}
+
+// One wave per token.  Its local routes are walked in k order; for each, the
+// wave streams dy[t] and out[q] in 8-column chunks, writes
+// d_out[q] = w * dy[t] (one fp32 product, rounded to the output format) and
+// sums dy * out in fp32, reduced across the wave for d_w[t,k].  Routes
+// without a local row get d_w = 0 and write no row.
+template <bool kDyF32, bool kOutF32, bool kDoF32>
+__global__ __launch_bounds__(kThreads) void combine_backward_kernel(
+    const uint8_t* __restrict__ dy, const uint8_t* __restrict__ out, const int32_t* __restrict__ slot_of,
+    const float* __restrict__ w, int T, int K, int H, int64_t rows_cap, uint8_t* __restrict__ d_out,
+    float* __restrict__ d_w) {
+  const int lane = moe::lane_id();
+  const int t = blockIdx.x * kWavesPerBlock + threadIdx.x / MOE_WAVE;
+  if (t >= T) return;
+  const int s_l = lane < K ? slot_of[static_cast<int64_t>(t) * K + lane] : -1;
+  const float w_l = lane < K ? w[static_cast<int64_t>(t) * K + lane] : 0.f;
+  const bool local = s_l >= 0 && s_l < rows_cap;
+  const uint64_t routes = __ballot(local);
+  const int nchunk = H / 8;
+  const uint8_t* dyrow = dy + static_cast<int64_t>(t) * H * (kDyF32 ? 4 : 2);
+  float dw_l = 0.f;
+  for (uint64_t m = routes; m; m &= m - 1) {
+    const int k = __builtin_ctzll(m);
+    const int q = __builtin_amdgcn_readlane(s_l, k);
+    const float wk = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w_l), k));
+    const uint8_t* orow = out + static_cast<int64_t>(q) * H * (kOutF32 ? 4 : 2);
+    uint8_t* drow = d_out + static_cast<int64_t>(q) * H * (kDoF32 ? 4 : 2);
+    float dot = 0.f;
+    for (int c = lane; c < nchunk; c += MOE_WAVE) {
+      float g[8], o[8], d[8];
+      load8<kDyF32>(dyrow, c, g);
+      load8<kOutF32>(orow, c, o);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        dot = fmaf(g[i], o[i], dot);
+        d[i] = wk * g[i];
+      }
+      store8<kDoF32>(drow, c, d);
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) dot += __shfl_xor(dot, off);
+    if (lane == k) dw_l = dot;
+  }
+  if (lane < K) d_w[static_cast<int64_t>(t) * K + lane] = dw_l;
+}
+
+// d_gate = dz * up * s * (1 + gate * (1 - s)), d_up = dz * SiLU(gate),
+// s = sigmoid(gate) from the hardware exp2 and reciprocal; one wave per valid
+// row, 4 columns per lane per step.
+template <bool kDzF32, bool kDgF32>
+__global__ __launch_bounds__(kThreads) void silu_mul_backward_kernel(
+    const float* __restrict__ g, const uint8_t* __restrict__ dz, const int32_t* __restrict__ counts,
+    const int32_t* __restrict__ offsets, int L, int64_t rows_cap, int I, uint8_t* __restrict__ dg) {
+  const int lane = moe::lane_id();
+  const int64_t q = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + threadIdx.x / MOE_WAVE;
+  if (q >= rows_cap) return;
+  // expert of row q: largest e with offsets[e] <= q; padding rows are skipped
+  int lo = 0, hi = L;
+  if (q < offsets[0]) return;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (offsets[mid] <= q) lo = mid; else hi = mid;
+  }
+  if (q >= static_cast<int64_t>(offsets[lo]) + counts[lo]) return;
+  const float* grow = g + q * 2 * I;
+  const uint8_t* zrow = dz + q * I * (kDzF32 ? 4 : 2);
+  uint8_t* drow = dg + q * 2 * I * (kDgF32 ? 4 : 2);
+  for (int c = lane; c < I / 4; c += MOE_WAVE) {
+    const float4 gt = reinterpret_cast<const float4*>(grow)[c];
+    const float4 up = reinterpret_cast<const float4*>(grow + I)[c];
+    float z[4];
+    if constexpr (kDzF32) {
+      const float4 v = reinterpret_cast<const float4*>(zrow)[c];
+      z[0] = v.x; z[1] = v.y; z[2] = v.z; z[3] = v.w;
+    } else {
+      const uint2 v = reinterpret_cast<const uint2*>(zrow)[c];
+      z[0] = __uint_as_float(v.x << 16); z[1] = __uint_as_float(v.x & 0xffff0000u);
+      z[2] = __uint_as_float(v.y << 16); z[3] = __uint_as_float(v.y & 0xffff0000u);
+    }
+    const float ga[4] = {gt.x, gt.y, gt.z, gt.w}, ua[4] = {up.x, up.y, up.z, up.w};
+    float dgate[4], dup[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float s = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(ga[i] * -1.44269504088896341f));
+      dup[i] = z[i] * (ga[i] * s);
+      dgate[i] = z[i] * ua[i] * s * (1.0f + ga[i] * (1.0f - s));
+    }
+    if constexpr (kDgF32) {
+      reinterpret_cast<float4*>(drow)[c] = make_float4(dgate[0], dgate[1], dgate[2], dgate[3]);
+      reinterpret_cast<float4*>(drow + I * 4)[c] = make_float4(dup[0], dup[1], dup[2], dup[3]);
+    } else {
+      reinterpret_cast<uint2*>(drow)[c] = make_uint2(
+          moe::f32_to_bf16(dgate[0]) | (uint32_t(moe::f32_to_bf16(dgate[1])) << 16),
+          moe::f32_to_bf16(dgate[2]) | (uint32_t(moe::f32_to_bf16(dgate[3])) << 16));
+      reinterpret_cast<uint2*>(drow + I * 2)[c] = make_uint2(
+          moe::f32_to_bf16(dup[0]) | (uint32_t(moe::f32_to_bf16(dup[1])) << 16),
+          moe::f32_to_bf16(dup[2]) | (uint32_t(moe::f32_to_bf16(dup[3])) << 16));
+    }
+  }
+}
+
+// w [L, N, K] -> wt [L, K, N], 64 x 64 element tiles through LDS (padded row
+// against bank conflicts); ESZ = element bytes (2 or 4).
+template <typename TE>
+__global__ __launch_bounds__(kThreads) void transpose_kernel(const TE* __restrict__ w, int N, int K,
+                                                            TE* __restrict__ wt) {
+  __shared__ TE tile[64][65];
+  const int e = blockIdx.z;
+  const int n0 = blockIdx.y * 64, k0 = blockIdx.x * 64;
+  const TE* src = w + static_cast<int64_t>(e) * N * K;
+  TE* dst = wt + static_cast<int64_t>(e) * N * K;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int r = ty; r < 64; r += kThreads / 64) {
+    const int n = n0 + r, k = k0 + tx;
+    if (n < N && k < K) tile[r][tx] = src[static_cast<int64_t>(n) * K + k];
+  }
+  __syncthreads();
+  for (int r = ty; r < 64; r += kThreads / 64) {
+    const int k = k0 + r, n = n0 + tx;
+    if (n < N && k < K) dst[static_cast<int64_t>(k) * N + n] = tile[tx][r];
+  }
+}
+
+}  // namespace
+
+extern "C" moe_status moe_combine_backward(const void* dy, moe_dtype dy_dt, const void* expert_out,
+                                           moe_dtype eo_dt, const int32_t* slot_of,
+                                           const float* topk_weights, int T, int K, int H, int64_t rows_cap,
+                                           void* d_out, moe_dtype d_out_dt, float* d_weights,
+                                           hipStream_t stream) {
+  MOE_CHECK(T >= 0 && K > 0 && H > 0 && rows_cap >= 0, MOE_ERR_INVALID_ARG);
+  MOE_CHECK(moe_host::valid_dtype(dy_dt) && moe_host::valid_dtype(eo_dt) && moe_host::valid_dtype(d_out_dt),
+            MOE_ERR_INVALID_ARG);
+  MOE_CHECK(dy_dt != MOE_FP8_E4M3 && eo_dt != MOE_FP8_E4M3 && d_out_dt != MOE_FP8_E4M3, MOE_ERR_UNSUPPORTED);
+  MOE_CHECK(H % 8 == 0 && K <= 64, MOE_ERR_UNSUPPORTED);
+  if (T == 0) return MOE_OK;
+  MOE_CHECK(dy && slot_of && topk_weights && d_weights && (rows_cap == 0 || (expert_out && d_out)),
+            MOE_ERR_INVALID_ARG);
+  const int grid = (T + kWavesPerBlock - 1) / kWavesPerBlock;
+  auto* g = static_cast<const uint8_t*>(dy);
+  auto* o = static_cast<const uint8_t*>(expert_out);
+  auto* d = static_cast<uint8_t*>(d_out);
+  const int sel = (dy_dt == MOE_F32 ? 4 : 0) | (eo_dt == MOE_F32 ? 2 : 0) | (d_out_dt == MOE_F32 ? 1 : 0);
+#define MOE_CB(A, B, C)                                                                                 \
+  combine_backward_kernel<A, B, C><<<grid, kThreads, 0, stream>>>(g, o, slot_of, topk_weights, T, K, H, \
+                                                                  rows_cap, d, d_weights)
+  switch (sel) {
+    case 0: MOE_CB(false, false, false); break;
+    case 1: MOE_CB(false, false, true); break;
+    case 2: MOE_CB(false, true, false); break;
+    case 3: MOE_CB(false, true, true); break;
+    case 4: MOE_CB(true, false, false); break;
+    case 5: MOE_CB(true, false, true); break;
+    case 6: MOE_CB(true, true, false); break;
+    default: MOE_CB(true, true, true); break;
+  }
+#undef MOE_CB
+  MOE_LAUNCH_CHECK();
+  return MOE_OK;
+}
+
+extern "C" moe_status moe_silu_mul_backward(const float* g, const void* dz, moe_dtype dz_dt,
+                                            const int32_t* counts, const int32_t* offsets, int L,
+                                            int64_t rows_cap, int I, void* dg, moe_dtype dg_dt,
+                                            hipStream_t stream) {
+  MOE_CHECK(L >= 1 && rows_cap >= 0 && I > 0, MOE_ERR_INVALID_ARG);
+  MOE_CHECK(moe_host::valid_dtype(dz_dt) && moe_host::valid_dtype(dg_dt), MOE_ERR_INVALID_ARG);
+  MOE_CHECK(dz_dt != MOE_FP8_E4M3 && dg_dt != MOE_FP8_E4M3, MOE_ERR_UNSUPPORTED);
+  MOE_CHECK(I % 4 == 0, MOE_ERR_UNSUPPORTED);
+  if (rows_cap == 0) return MOE_OK;
+  MOE_CHECK(g && dz && dg && counts && offsets, MOE_ERR_INVALID_ARG);
+  const int64_t grid64 = (rows_cap + kWavesPerBlock - 1) / kWavesPerBlock;
+  MOE_CHECK(grid64 <= 0x7fffffff, MOE_ERR_UNSUPPORTED);
+  const int grid = static_cast<int>(grid64);
+  auto* z = static_cast<const uint8_t*>(dz);
+  auto* d = static_cast<uint8_t*>(dg);
+  if (dz_dt == MOE_F32 && dg_dt == MOE_F32)
+    silu_mul_backward_kernel<true, true><<<grid, kThreads, 0, stream>>>(g, z, counts, offsets, L, rows_cap, I, d);
+  else if (dz_dt == MOE_F32)
+    silu_mul_backward_kernel<true, false><<<grid, kThreads, 0, stream>>>(g, z, counts, offsets, L, rows_cap, I, d);
+  else if (dg_dt == MOE_F32)
+    silu_mul_backward_kernel<false, true><<<grid, kThreads, 0, stream>>>(g, z, counts, offsets, L, rows_cap, I, d);
+  else
+    silu_mul_backward_kernel<false, false><<<grid, kThreads, 0, stream>>>(g, z, counts, offsets, L, rows_cap, I, d);
+  MOE_LAUNCH_CHECK();
+  return MOE_OK;
+}
+
+extern "C" moe_status moe_transpose_weights(const void* w, moe_dtype w_dt, int L, int N, int K, void* wt,
+                                            hipStream_t stream) {
+  MOE_CHECK(L >= 1 && N > 0 && K > 0 && moe_host::valid_dtype(w_dt), MOE_ERR_INVALID_ARG);
+  MOE_CHECK(w_dt != MOE_FP8_E4M3, MOE_ERR_UNSUPPORTED);
+  MOE_CHECK(w && wt && w != wt, MOE_ERR_INVALID_ARG);
+  MOE_CHECK(L <= 65535, MOE_ERR_UNSUPPORTED);
+  const dim3 grid((K + 63) / 64, (N + 63) / 64, L);
+  if (w_dt == MOE_F32)
+    transpose_kernel<float><<<grid, kThreads, 0, stream>>>(static_cast<const float*>(w), N, K,
+                                                           static_cast<float*>(wt));
+  else
+    transpose_kernel<uint16_t><<<grid, kThreads, 0, stream>>>(static_cast<const uint16_t*>(w), N, K,
+                                                              static_cast<uint16_t*>(wt));
+  MOE_LAUNCH_CHECK();
+  return MOE_OK;
+}

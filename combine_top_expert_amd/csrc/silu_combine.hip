@@ -100,7 +100,8 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const uint8_t* __rest
   // lane k holds route k of the token; the routes with a local row form a
   // bit mask in k order (ballot bit k = lane k)
   const int s_l = lane < K ? slot_of[static_cast<int64_t>(t) * K + lane] : -1;
-  const float w_l = lane < K ? w[static_cast<int64_t>(t) * K + lane] : 0.f;
+  // null weights: every route weighs 1 (permute backward); 1 * v is exact
+  const float w_l = lane < K ? (w != nullptr ? w[static_cast<int64_t>(t) * K + lane] : 1.f) : 0.f;
   uint64_t m = __ballot(s_l >= 0 && s_l < rows_cap);
   const int nchunk = H / 8;
   const int c0 = p * kPartChunks + lane;         // chunk u of this lane: c0 + 64u
@@ -217,15 +218,17 @@ extern "C" moe_status moe_silu_mul(const float* g, const int32_t* counts, const 
   return MOE_OK;
 }
 
-extern "C" moe_status moe_combine(const void* expert_out, moe_dtype eo_dt, const int32_t* slot_of,
-                                  const float* topk_weights, int T, int K, int H, int64_t rows_cap,
-                                  void* y, moe_dtype y_dt, hipStream_t stream) {
+namespace {
+
+moe_status combine_launch(const void* expert_out, moe_dtype eo_dt, const int32_t* slot_of,
+                          const float* topk_weights, int T, int K, int H, int64_t rows_cap, void* y,
+                          moe_dtype y_dt, hipStream_t stream) {
   MOE_CHECK(T >= 0 && K > 0 && H > 0 && rows_cap >= 0, MOE_ERR_INVALID_ARG);
   MOE_CHECK(moe_host::valid_dtype(eo_dt) && moe_host::valid_dtype(y_dt), MOE_ERR_INVALID_ARG);
   MOE_CHECK(eo_dt != MOE_FP8_E4M3 && y_dt != MOE_FP8_E4M3, MOE_ERR_UNSUPPORTED);
   MOE_CHECK(H % 8 == 0 && K <= kMaxK, MOE_ERR_UNSUPPORTED);
   if (T == 0) return MOE_OK;
-  MOE_CHECK(slot_of && topk_weights && y && (rows_cap == 0 || expert_out), MOE_ERR_INVALID_ARG);
+  MOE_CHECK(slot_of && y && (rows_cap == 0 || expert_out), MOE_ERR_INVALID_ARG);
   const int parts = (H / 8 + kPartChunks - 1) / kPartChunks;
   const int64_t grid64 = (static_cast<int64_t>(T) * parts + kRowsPerBlock - 1) / kRowsPerBlock;
   MOE_CHECK(grid64 <= 0x7fffffff, MOE_ERR_UNSUPPORTED);
@@ -243,4 +246,19 @@ extern "C" moe_status moe_combine(const void* expert_out, moe_dtype eo_dt, const
     combine_kernel<false, false><<<grid, kThreads, 0, stream>>>(eo, slot_of, topk_weights, T, K, H, rows_cap, yo, parts);
   MOE_LAUNCH_CHECK();
   return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" moe_status moe_combine(const void* expert_out, moe_dtype eo_dt, const int32_t* slot_of,
+                                  const float* topk_weights, int T, int K, int H, int64_t rows_cap,
+                                  void* y, moe_dtype y_dt, hipStream_t stream) {
+  MOE_CHECK(T == 0 || topk_weights, MOE_ERR_INVALID_ARG);
+  return combine_launch(expert_out, eo_dt, slot_of, topk_weights, T, K, H, rows_cap, y, y_dt, stream);
+}
+
+extern "C" moe_status moe_permute_backward(const void* d_buf, moe_dtype d_buf_dt, const int32_t* slot_of,
+                                           int T, int K, int H, int64_t rows_cap, void* dx, moe_dtype dx_dt,
+                                           hipStream_t stream) {
+  return combine_launch(d_buf, d_buf_dt, slot_of, nullptr, T, K, H, rows_cap, dx, dx_dt, stream);
 }

@@ -19,6 +19,8 @@ import torch
 from . import (MOE_EPI_SILU_MUL, MOE_EPI_STORE_G, moe_combine, moe_dispatch_layout,
                moe_dispatch_layout_workspace_bytes, moe_grouped_gemm_w2, moe_grouped_gemm_w13,
                moe_grouped_gemm_workspace_bytes, moe_pack_w13, MOE_W_PACKED, MOE_W_ROW_MAJOR,
+               moe_combine_backward, moe_silu_mul_backward, moe_permute_backward,
+               moe_transpose_weights,
                moe_permute, moe_silu_mul)
 
 _TORCH = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8}
@@ -127,6 +129,50 @@ class MoELayer:
 
     def combine(self, topk_weights):
         moe_combine(self.out, self.slot_of, topk_weights, self.y)
+
+    # ---- backward (bf16 / fp32 layers)
+    def prepare_backward(self):
+        """Transposed weights and gradient buffers, made once (the weights are
+        transposed again whenever set_weights is called)."""
+        s = self.shape
+        if s.wdt == "fp8":
+            raise ValueError("the backward covers bf16 and fp32 layers")
+        dev = self.buf.device
+        gdt = self.out.dtype                       # gradients stored like the expert output
+        if getattr(self, "_wt_src", None) is not (self.w13, self.w2):
+            self.w2_t = torch.empty(s.L, s.I, s.H, dtype=self.w2.dtype, device=dev)
+            self.w13_t = torch.empty(s.L, s.H, 2 * s.I, dtype=self.w13.dtype, device=dev)
+            moe_transpose_weights(self.w2, self.w2_t)
+            moe_transpose_weights(self.w13, self.w13_t)
+            self._wt_src = (self.w13, self.w2)
+        rc = s.rows_cap
+        if getattr(self, "d_out", None) is None:
+            self.d_out = torch.empty(rc, s.H, dtype=gdt, device=dev)
+            self.d_w = torch.empty(s.T, s.K, dtype=torch.float32, device=dev)
+            self.g_saved = torch.empty(rc, 2 * s.I, dtype=torch.float32, device=dev)
+            self.dz = torch.empty(rc, s.I, dtype=gdt, device=dev)
+            self.dg = torch.empty(rc, 2 * s.I, dtype=gdt, device=dev)
+            self.da = torch.empty(rc, s.H, dtype=gdt, device=dev)
+            self.dx = torch.empty(s.T, s.H, dtype=gdt, device=dev)
+
+    def backward(self, dy, topk_weights):
+        """Gradients of the last forward for dy [T,H]: returns (dx [T,H],
+        d_w [T,K]).  Reuses the forward's routing (slot_of, counts, offsets),
+        its permuted activations and expert outputs; G is recomputed."""
+        self.prepare_backward()
+        moe_combine_backward(dy, self.out, self.slot_of, topk_weights, self.d_out, self.d_w)
+        moe_grouped_gemm_w2(self.d_out, None, self.w2_t, None, self.counts, self.offsets, self.dz,
+                            workspace=self.gemm_workspace)
+        w, lay = ((self.w13_packed, MOE_W_PACKED) if self.w13_packed is not None
+                  else (self.w13, MOE_W_ROW_MAJOR))
+        moe_grouped_gemm_w13(self.buf, self.buf_scales, w, self.w13_scales, self.counts,
+                             self.offsets, MOE_EPI_STORE_G, self.g_saved,
+                             workspace=self.gemm_workspace, w13_layout=lay)
+        moe_silu_mul_backward(self.g_saved, self.dz, self.counts, self.offsets, self.dg)
+        moe_grouped_gemm_w2(self.dg, None, self.w13_t, None, self.counts, self.offsets, self.da,
+                            workspace=self.gemm_workspace)
+        moe_permute_backward(self.da, self.slot_of, self.dx)
+        return self.dx, self.d_w
 
     def forward(self, x, topk_ids, topk_weights):
         """The whole path on the current stream; returns y [T,H] (no sync)."""

@@ -5,10 +5,13 @@
  *   moe_dispatch_layout -> moe_permute -> moe_grouped_gemm_w13
  *     -> (moe_silu_mul) -> moe_grouped_gemm_w2 -> moe_combine
  *
+ * and its backward (the end of this file).
+ *
  * Pages cited (by title):
  *   [EP]  "SGLang、NCCL 与 MoE EP：从职责边界到执行机制"
  *   [ECB] "SGLang Expert Compute Backend：从接收布局到 Triton 专家计算"
  *   [DEP] "DeepEP 架构与实现笔记"
+ *   [XT]  "XTuner Domino EP"
  *
  * Conventions shared by every entry point
  *   - Every pointer argument is DEVICE memory owned by the caller; the
@@ -77,7 +80,8 @@ typedef enum moe_weight_layout {
 const char* moe_status_string(int status);
 
 /* ABI version; bumped on any signature change or added entry point (2: moe_router_topk;
- * 3: GEMM workspace for the K-split last round; 4: moe_pack_w13 and the W13 layout). */
+ * 3: GEMM workspace for the K-split last round; 4: moe_pack_w13 and the W13 layout;
+ * 5: the backward entry points). */
 int moe_abi_version(void);
 
 /* Bytes of device workspace moe_dispatch_layout needs for (T, K, L). */
@@ -275,6 +279,74 @@ moe_status moe_combine(const void* expert_out, moe_dtype eo_dt, const int32_t* s
 moe_status moe_router_topk(const float* logits, const float* bias, int T, int E, int K,
                            int bias_in_weights, int32_t* topk_ids, float* topk_weights,
                            hipStream_t stream);
+
+/* ---------------------------------------------------------------- backward
+ *
+ * The gradients of the path, consumed in the reverse order of the forward
+ * ([XT] "XTuner Domino EP": the DeepEP part's complete run path consumes the
+ * saved routing -- here slot_of, counts, offsets -- in reverse; the UltraEP
+ * part's backward runs combine backward, the grouped GEMMs' gradients and the
+ * inverse permutation).  Formulas: the derivatives of the forward ([EP] §1.1,
+ * [ECB] §1.1, §3.6).  bf16 and fp32 data only.  Per GPU share, a route without
+ * a local row contributes nothing: its d_w is 0 and it writes no row.
+ *
+ *   d_out = combine_backward(dy)            moe_combine_backward (also d_w)
+ *   dZ    = d_out W2[e]                     moe_grouped_gemm_w2 on W2^T [L,I,H]
+ *   G     = A W13[e]^T  (recomputed)        moe_grouped_gemm_w13, MOE_EPI_STORE_G
+ *   dG    = silu_mul_backward(G, dZ)        moe_silu_mul_backward
+ *   dA    = dG W13[e]                       moe_grouped_gemm_w2 on W13^T [L,H,2I]
+ *   dx    = permute_backward(dA)            moe_permute_backward
+ *
+ * moe_grouped_gemm_w2 computes rows * W^T for any [L, N, K] weights (N = its
+ * H argument, K = its I argument), so with the transposes written once by
+ * moe_transpose_weights it is the data gradient of both GEMMs.
+ */
+
+/*
+ * moe_combine_backward -- the gradient of moe_combine.
+ *   d_out[q]   = topk_weights[t,k] * dy[t]   (one fp32 product, rounded to
+ *                d_out_dt) for every local route q = slot_of[t,k]
+ *   d_weights[t,k] = sum_h dy[t,h] * expert_out[q,h] (fp32 accumulation),
+ *                0 for a route without a local row
+ *   dy [T,H] (dy_dt), expert_out [rows_cap,H] (eo_dt, the forward's output),
+ *   d_out [rows_cap,H] (padding rows untouched), d_weights [T,K] fp32.
+ * dtypes: F32 or BF16.  Limits: H % 8 == 0, K <= 64.
+ */
+moe_status moe_combine_backward(const void* dy, moe_dtype dy_dt, const void* expert_out,
+                                moe_dtype eo_dt, const int32_t* slot_of, const float* topk_weights,
+                                int T, int K, int H, int64_t rows_cap, void* d_out,
+                                moe_dtype d_out_dt, float* d_weights, hipStream_t stream);
+
+/*
+ * moe_silu_mul_backward -- the gradient of Z = SiLU(gate) * up on valid rows:
+ *   d_gate = dZ * up * s * (1 + gate * (1 - s)),  d_up = dZ * SiLU(gate),
+ *   s = sigmoid(gate), fp32 (hardware exp2 / reciprocal), rounded to dg_dt.
+ *   g [rows_cap,2I] fp32 (the forward's G); dz [rows_cap,I] (dz_dt);
+ *   dg [rows_cap,2I] (dg_dt: d_gate in columns [0,I), d_up in [I,2I)).
+ * dtypes: F32 or BF16.  Limits: I % 4 == 0.
+ */
+moe_status moe_silu_mul_backward(const float* g, const void* dz, moe_dtype dz_dt,
+                                 const int32_t* counts, const int32_t* offsets, int L,
+                                 int64_t rows_cap, int I, void* dg, moe_dtype dg_dt,
+                                 hipStream_t stream);
+
+/*
+ * moe_permute_backward -- the gradient of moe_permute (an unweighted combine):
+ *   dx[t] = sum over local routes k, in increasing k, of d_buf[slot_of[t,k]]
+ *   (fp32, rounded to dx_dt); 0 for a token without a local route.
+ *   d_buf [rows_cap,H] (d_buf_dt), dx [T,H] (dx_dt).  dtypes: F32 or BF16.
+ * Limits: H % 8 == 0, K <= 64.
+ */
+moe_status moe_permute_backward(const void* d_buf, moe_dtype d_buf_dt, const int32_t* slot_of,
+                                int T, int K, int H, int64_t rows_cap, void* dx, moe_dtype dx_dt,
+                                hipStream_t stream);
+
+/*
+ * moe_transpose_weights -- wt[e] = w[e]^T: w [L,N,K] -> wt [L,K,N] (same
+ * dtype, F32 or BF16), caller-owned, non-overlapping; once per weight update.
+ */
+moe_status moe_transpose_weights(const void* w, moe_dtype w_dt, int L, int N, int K, void* wt,
+                                 hipStream_t stream);
 
 #ifdef __cplusplus
 }

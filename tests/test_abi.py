@@ -35,9 +35,10 @@ def test_header_declares_the_entry_points():
     fns = declared_functions()
     for name in ["moe_dispatch_layout", "moe_permute", "moe_grouped_gemm_w13", "moe_silu_mul",
                  "moe_grouped_gemm_w2", "moe_combine", "moe_router_topk",
-                 "moe_grouped_gemm_workspace_bytes", "moe_pack_w13"]:
+                 "moe_grouped_gemm_workspace_bytes", "moe_pack_w13", "moe_combine_backward",
+                 "moe_silu_mul_backward", "moe_permute_backward", "moe_transpose_weights"]:
         assert name in fns
-    assert len(fns) == 12
+    assert len(fns) == 16
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -56,7 +57,7 @@ def test_status_strings_and_version(lib):
     assert lib.moe_status_string(0) == b"MOE_OK"
     assert lib.moe_status_string(-2) == b"MOE_ERR_UNSUPPORTED"
     assert lib.moe_status_string(12345) == b"MOE_ERR_UNKNOWN"
-    assert lib.moe_abi_version() == 4
+    assert lib.moe_abi_version() == 5
 
 
 def test_workspace_bytes(lib):
@@ -177,7 +178,7 @@ def test_python_binding_loads_and_matches_header(lib):
     import combine_top_expert_amd as ep
     for name in declared_functions():
         assert callable(getattr(ep, name)), name
-    assert ep.moe_abi_version() == 4
+    assert ep.moe_abi_version() == 5
     assert ep.moe_status_string(-1) == "MOE_ERR_INVALID_ARG"
 
 
@@ -208,3 +209,35 @@ def test_router_argument_errors(lib):
     assert r(P(), None, 4, 256, 65, 1, P(), P(), None) == UNSUPPORTED   # K > 64
     assert r(None, None, 4, 256, 8, 1, P(), P(), None) == INVALID       # no logits
     assert r(None, None, 0, 256, 8, 1, None, None, None) == OK          # T = 0
+
+
+def test_backward_argument_errors(lib):
+    cb = lib.moe_combine_backward
+    cb.restype = ctypes.c_int
+    cb.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
+                   ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int64,
+                   ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    assert cb(P(), 1, P(), 1, P(), P(), 4, 2, 100, 8, P(), 1, P(), None) == UNSUPPORTED  # H % 8
+    assert cb(P(), 2, P(), 1, P(), P(), 4, 2, 256, 8, P(), 1, P(), None) == UNSUPPORTED  # fp8 dy
+    assert cb(P(), 1, P(), 1, P(), None, 4, 2, 256, 8, P(), 1, P(), None) == INVALID     # no weights
+    assert cb(None, 1, None, 1, None, None, 0, 2, 256, 8, None, 1, None, None) == OK     # T = 0
+    sb = lib.moe_silu_mul_backward
+    sb.restype = ctypes.c_int
+    sb.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                   ctypes.c_int, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    assert sb(P(), P(), 1, P(), P(), 2, 256, 126, P(), 1, None) == UNSUPPORTED            # I % 4
+    assert sb(P(), P(), 2, P(), P(), 2, 256, 128, P(), 1, None) == UNSUPPORTED            # fp8 dz
+    assert sb(None, P(), 1, P(), P(), 2, 256, 128, P(), 1, None) == INVALID
+    pb = lib.moe_permute_backward
+    pb.restype = ctypes.c_int
+    pb.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                   ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    assert pb(P(), 1, P(), 4, 65, 256, 8, P(), 1, None) == UNSUPPORTED                   # K > 64
+    assert pb(P(), 1, None, 4, 2, 256, 8, P(), 1, None) == INVALID
+    tw = lib.moe_transpose_weights
+    tw.restype = ctypes.c_int
+    tw.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                   ctypes.c_void_p, ctypes.c_void_p]
+    assert tw(P(), 2, 2, 128, 128, P(8), None) == UNSUPPORTED                            # fp8
+    assert tw(P(), 1, 2, 128, 128, P(), None) == INVALID                                 # in place
+    assert tw(P(), 1, 0, 128, 128, P(8), None) == INVALID
