@@ -26,6 +26,8 @@ so, for an upstream gradient dy [T, H]:
   d_gate    = dZ * up * s * (1 + gate * (1 - s)),    s = sigmoid(gate)
   dA[q]     = [d_gate | d_up] W13[e]                 (data gradient of the gate/up GEMM)
   dx[t]     = sum_{k local} dA[q(t,k)]               (permute backward, an unweighted combine)
+  dW2[e]    = sum_{q of e} d_out[q]^T Z[q]            (weight gradient of the down GEMM)
+  dW13[e]   = sum_{q of e} [d_gate | d_up][q]^T A[q]  (weight gradient of the gate/up GEMM)
 
 Readings:
   * one GPU's share: routes with no local row contribute nothing here, so
@@ -35,7 +37,9 @@ Readings:
   * every gradient that the next step consumes is rounded to the storage
     format of the configuration (bf16 or fp32) before it is consumed, as the
     GPU path stores it;
-  * G is the forward's fp32 G (the GPU path recomputes it with the gate/up GEMM).
+  * G is the forward's fp32 G (the GPU path recomputes it with the gate/up GEMM);
+  * weight gradients reduce over the expert's valid rows in float64 and are
+    rounded once to fp32; an expert without rows gets zeros.
 """
 from __future__ import annotations
 
@@ -98,6 +102,14 @@ def permute_backward(d_rows: dict, slot_of: np.ndarray, H: int, dx_dt: str) -> n
     return to_format(dx, dx_dt)
 
 
+def wgrad(b_rows: np.ndarray, a_rows: np.ndarray, N: int, K: int) -> np.ndarray:
+    """C = B^T A over one expert's rows: B [m, N], A [m, K] -> [N, K], float64
+    products rounded once to fp32 (zeros for m = 0)."""
+    if len(b_rows) == 0:
+        return np.zeros((N, K), np.float32)
+    return (np.asarray(b_rows, np.float64).T @ np.asarray(a_rows, np.float64)).astype(np.float32)
+
+
 def layer_backward(wl, dy: np.ndarray, ew) -> dict:
     """The whole backward for a workload (bf16 or fp32 weights): forward
     quantities recomputed by the forward oracle's own steps, then the steps
@@ -117,6 +129,8 @@ def layer_backward(wl, dy: np.ndarray, ew) -> dict:
     fwd = expert_mlp_rows(cfg, a_by, e_of, ew)
     d_out, d_w = combine_backward(dy, fwd["out"], slot_of, wl.weights, gdt)
     dz, dg, da = {}, {}, {}
+    dw2 = np.zeros((cfg.L, cfg.H, cfg.I), np.float32)
+    dw13 = np.zeros((cfg.L, 2 * cfg.I, cfg.H), np.float32)
     by_e: dict[int, list] = {}
     for q, e in e_of.items():
         by_e.setdefault(e, []).append(q)
@@ -127,11 +141,15 @@ def layer_backward(wl, dy: np.ndarray, ew) -> dict:
         g_e = np.stack([fwd["G"][q] for q in qs])
         dg_e = to_format(silu_mul_backward(g_e, dz_e), gdt)
         da_e = to_format((dg_e.astype(np.float64) @ ew.w13(e)).astype(np.float32), gdt)
+        z_e = buffer_values(np.stack([fwd["Z"][q] for q in qs]), cfg.z_dt,
+                            np.stack([fwd["Zs"][q] for q in qs]) if fwd["Zs"] else None)
+        dw2[e] = wgrad(do, z_e, cfg.H, cfg.I)
+        dw13[e] = wgrad(dg_e, np.stack([a_by[q] for q in qs]), 2 * cfg.I, cfg.H)
         for i, q in enumerate(qs):
             dz[q], dg[q], da[q] = dz_e[i], dg_e[i], da_e[i]
     dx = permute_backward(da, slot_of, cfg.H, gdt)
     return {"layout": lay, "rows": rows, "fwd": fwd, "d_out": d_out, "d_w": d_w, "dz": dz,
-            "dg": dg, "da": da, "dx": dx, "e_of": e_of}
+            "dg": dg, "da": da, "dx": dx, "e_of": e_of, "dw2": dw2, "dw13": dw13}
 
 
 def gemm_w13_rows(a_by: dict, e_of: dict, ew) -> dict:

@@ -7,7 +7,8 @@ share none of its code:
 * central finite differences of SiLU(gate) * up in float64 pin
   silu_mul_backward;
 * an explicit 0/1 permutation matrix pins permute_backward and the dispatch
-  half of combine_backward.
+  half of combine_backward;
+* autograd's gradients of the dense forward's expert weights pin dW2, dW13.
 Shapes include non-local experts (a share of L < E experts) and tokens with
 no local route."""
 import numpy as np
@@ -22,12 +23,15 @@ from workloads import get_config, make_workload
 pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
 
 
-def _dense_forward_backward(wl, dy):
-    """float64 autograd of y[t] = sum_{k: local} w[t,k] * F_e(x[t])."""
+def _dense_forward_backward(wl, dy, weight_grads=False):
+    """float64 autograd of y[t] = sum_{k: local} w[t,k] * F_e(x[t]); with
+    weight_grads also d/dW13[e] and d/dW2[e]."""
     cfg = wl.cfg
     ew = moe.ExpertWeights(cfg, wl.w)
     x = torch.tensor(moe.x_values(wl.x, cfg.act), dtype=torch.float64, requires_grad=True)
     w = torch.tensor(np.asarray(wl.weights, np.float64), requires_grad=True)
+    W13 = [torch.tensor(ew.w13(e), requires_grad=weight_grads) for e in range(cfg.L)]
+    W2 = [torch.tensor(ew.w2(e), requires_grad=weight_grads) for e in range(cfg.L)]
     T, K = wl.ids.shape
     y = torch.zeros(T, cfg.H, dtype=torch.float64)
     rows = []
@@ -39,12 +43,15 @@ def _dense_forward_backward(wl, dy):
                 continue
             rows.append((t, k, e))
     for t, k, e in rows:
-        w13 = torch.tensor(ew.w13(e))
-        w2 = torch.tensor(ew.w2(e))
-        gu = x[t] @ w13.T
+        gu = x[t] @ W13[e].T
         z = torch.nn.functional.silu(gu[:cfg.I]) * gu[cfg.I:]
-        y[t] = y[t] + w[t, k] * (z @ w2.T)
+        y[t] = y[t] + w[t, k] * (z @ W2[e].T)
     y.backward(torch.tensor(dy, dtype=torch.float64))
+    if weight_grads:
+        zero = lambda t, shape: (t.grad.numpy() if t.grad is not None else np.zeros(shape))
+        return (x.grad.numpy(), w.grad.numpy(),
+                np.stack([zero(W13[e], W13[e].shape) for e in range(cfg.L)]),
+                np.stack([zero(W2[e], W2[e].shape) for e in range(cfg.L)]))
     return x.grad.numpy(), w.grad.numpy()
 
 
@@ -77,6 +84,35 @@ def test_layer_backward_matches_autograd(which):
     if which == "share":
         no_local = ~(res["layout"]["slot_of"] >= 0).any(axis=1)
         assert no_local.any() and np.all(res["dx"][no_local] == 0)
+
+
+@pytest.mark.parametrize("which", ["toy_fp32", "share"])
+def test_weight_gradients_match_autograd(which):
+    """dW2, dW13 of the oracle against autograd's gradients of the dense
+    forward's weights (experts without rows: zeros on both sides)."""
+    cfg = _share_config() if which == "share" else get_config(which)
+    wl = make_workload(cfg)
+    rng = np.random.default_rng(6)
+    dy = rng.standard_normal((cfg.T, cfg.H)).astype(np.float32)
+    res = B.layer_backward(wl, dy, moe.ExpertWeights(cfg, wl.w))
+    _, _, dw13_ref, dw2_ref = _dense_forward_backward(wl, dy, weight_grads=True)
+    for got, ref in ((res["dw2"], dw2_ref), (res["dw13"], dw13_ref)):
+        assert got.shape == ref.shape
+        err = np.linalg.norm(got - ref) / np.linalg.norm(ref)
+        assert err < 2e-6, err
+        for e in range(cfg.L):
+            if not np.any(ref[e]):
+                assert not np.any(got[e])
+
+
+def test_wgrad_closed_form():
+    rng = np.random.default_rng(1)
+    b = rng.standard_normal((7, 5))
+    a = rng.standard_normal((7, 3))
+    c = B.wgrad(b, a, 5, 3)
+    ref = np.array([[sum(b[r, n] * a[r, k] for r in range(7)) for k in range(3)] for n in range(5)])
+    np.testing.assert_allclose(c, ref, rtol=1e-6)
+    assert not np.any(B.wgrad(np.zeros((0, 5)), np.zeros((0, 3)), 5, 3))
 
 
 def test_autograd_pin_catches_planted_mistakes():
