@@ -35,6 +35,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="prefill_fp8")
     ap.add_argument("--cpu-sample-tokens", type=int, default=8192)
+    ap.add_argument("--skip-backward", action="store_true",
+                    help="do not time the backward (bf16 / fp32 workloads)")
     ap.add_argument("--skip-cpu-baseline", action="store_true",
                     help="omit the oracle timing (profiling runs)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -147,6 +149,55 @@ def router_timing(cfg, steps, dev):
     nbytes = cfg.T * cfg.E * 4 + cfg.E * 4 + cfg.T * cfg.K * 8
     return {"us": us, "bytes": nbytes, "gbs": nbytes / (us * 1e-6) / 1e9,
             "shape": {"T": cfg.T, "E": cfg.E, "K": cfg.K, "bias": cfg.bias}}
+
+
+def backward_timing(cfg, layer, w, steps, dev):
+    """The layer's backward (bf16 / fp32 weights) after the timed forward:
+    each stage timed with events around it over ``steps`` passes (medians).
+    GEMM stages report TFLOP/s, streaming stages GB/s of algorithmic bytes."""
+    import torch
+
+    g = torch.Generator(device=dev)
+    g.manual_seed(cfg.seed + 17)
+    gb = {"bf16": 2, "f32": 4}[cfg.out_dt]
+    dy = torch.randn(cfg.T, cfg.H, device=dev, generator=g).to(layer.out.dtype)
+    st = layer.backward_stages(dy, w)
+    for _ in range(3):
+        for _, f in st:
+            f()
+    stream = torch.cuda.current_stream(dev)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(st) + 1)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for s in range(steps):
+        ev[s][0].record(stream)
+        for i, (_, f) in enumerate(st):
+            f()
+            ev[s][i + 1].record(stream)
+    torch.cuda.synchronize()
+    per = np.array([[ev[s][i].elapsed_time(ev[s][i + 1]) for i in range(len(st))]
+                    for s in range(steps)]) * 1e3                     # us
+    us = {name: float(np.median(per[:, i])) for i, (name, _) in enumerate(st)}
+    rows = int(layer.counts.cpu().numpy().sum())
+    T, K, H, I = cfg.T, cfg.K, cfg.H, cfg.I
+    tok_local = int((layer.slot_of.cpu().numpy() >= 0).any(axis=1).sum())
+    flops = {"gemm_dz": 2 * rows * H * I, "gemm_g": 4 * rows * H * I, "gemm_da": 4 * rows * H * I,
+             "wgrad_w2": 2 * rows * H * I, "wgrad_w13": 4 * rows * H * I}
+    nbytes = {
+        # dy once per token with a local route, out rows in, d_out rows out, ids/weights/d_w
+        "combine_bw": tok_local * H * gb + 2 * rows * H * gb + T * K * 12,
+        # G (fp32) and dZ in, dG out
+        "silu_mul_bw": rows * 2 * I * 4 + rows * I * gb + rows * 2 * I * gb,
+        # dA rows in, dx out, ids
+        "permute_bw": rows * H * gb + T * H * gb + T * K * 4,
+    }
+    peak = MFMA_PEAK_TFLOPS[cfg.wdt]
+    res = {"us": us, "total_us": float(np.median(per.sum(axis=1))), "rows": rows,
+           "timing": "medians over the passes, an event between stages",
+           "tflops": {k: v / (us[k] * 1e-6) / 1e12 for k, v in flops.items()},
+           "gbs": {k: v / (us[k] * 1e-6) / 1e9 for k, v in nbytes.items()}}
+    res["mfma_frac"] = {k: v / peak for k, v in res["tflops"].items()}
+    res["hbm_frac"] = {k: v / HBM_PEAK_GBS for k, v in res["gbs"].items()}
+    return res
 
 
 def main():
@@ -305,8 +356,12 @@ def main():
     out["stage_gbs"] = {"permute": perm_bytes / (stage_us["permute"] * 1e-6) / 1e9,
                         "combine": comb_bytes / (stage_us["combine"] * 1e-6) / 1e9}
 
+    out["next_rows"] = {}
     if cfg.routing == "softmax":
-        out["next_rows"] = {"router_topk": router_timing(cfg, args.steps, dev)}
+        out["next_rows"]["router_topk"] = router_timing(cfg, args.steps, dev)
+    if cfg.wdt != "fp8" and not args.skip_backward:
+        print("[bench] backward stages", file=sys.stderr, flush=True)
+        out["next_rows"]["backward"] = backward_timing(cfg, layer, w, min(args.steps, 20), dev)
     if not args.skip_cpu_baseline:
         print("[bench] cpu baseline (oracle sample)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_sample_tokens)

@@ -21,7 +21,7 @@ __all__ = [
     "moe_status_string", "moe_abi_version", "moe_dispatch_layout_workspace_bytes",
     "moe_grouped_gemm_workspace_bytes", "moe_pack_w13", "MOE_W_ROW_MAJOR", "MOE_W_PACKED",
     "moe_combine_backward", "moe_silu_mul_backward", "moe_permute_backward", "moe_transpose_weights",
-    "moe_dispatch_layout", "moe_permute", "moe_grouped_gemm_w13", "moe_silu_mul",
+    "moe_grouped_gemm_wgrad", "moe_dispatch_layout", "moe_permute", "moe_grouped_gemm_w13", "moe_silu_mul",
     "moe_grouped_gemm_w2", "moe_combine", "moe_router_topk", "dtype_code",
 ]
 
@@ -57,6 +57,7 @@ _SIG = {
     "moe_silu_mul_backward": (_i, [_p, _p, _i, _p, _p, _i, _i64, _i, _p, _i, _p]),
     "moe_permute_backward": (_i, [_p, _i, _p, _i, _i, _i, _i64, _p, _i, _p]),
     "moe_transpose_weights": (_i, [_p, _i, _i, _i, _i, _p, _p]),
+    "moe_grouped_gemm_wgrad": (_i, [_p, _p, _i, _p, _p, _i, _i64, _i, _i, _p, _p]),
 }
 for _name, (_res, _args) in _SIG.items():
     if not hasattr(lib, _name):
@@ -258,3 +259,16 @@ def moe_transpose_weights(w, wt) -> None:
         raise ValueError("wt must be [L,K,N] of w's dtype")
     _check("moe_transpose_weights", lib.moe_transpose_weights(
         _ptr(w, "w"), dtype_code(w), L, N, K, _ptr(wt, "wt"), _stream(w)))
+
+
+def moe_grouped_gemm_wgrad(b, a, counts, offsets, c) -> None:
+    """b [rows_cap,N], a [rows_cap,K] (same dtype) -> c [L,N,K] fp32 with
+    c[e] = sum over expert e's valid rows of b^T a."""
+    rows_cap, N = b.shape
+    K = a.shape[1]
+    L = counts.shape[0]
+    if a.shape[0] != rows_cap or a.dtype != b.dtype or tuple(c.shape) != (L, N, K):
+        raise ValueError("wgrad needs b [R,N], a [R,K] of one dtype and c [L,N,K]")
+    _check("moe_grouped_gemm_wgrad", lib.moe_grouped_gemm_wgrad(
+        _ptr(b, "b"), _ptr(a, "a"), dtype_code(b), _i32(counts, "counts"), _i32(offsets, "offsets"),
+        L, rows_cap, N, K, _f32(c, "c"), _stream(b)))

@@ -181,7 +181,142 @@ __global__ __launch_bounds__(kThreads) void transpose_kernel(const TE* __restric
   }
 }
 
+// ---------------------------------------------------------------- weight gradients
+// C[e] = B_e^T A_e over expert e's valid rows: B [rows_cap, N], A [rows_cap, K]
+// -> C [L, N, K] fp32.  One workgroup per (expert, 128 x 128 tile of C);
+// rows are reduced in chunks of 32.  Each chunk of B (32 x 128) and A
+// (32 x 128) is staged into LDS transposed ([column][row], rows contiguous)
+// so that a matrix-core operand -- 8 consecutive rows of one column -- is one
+// 16-byte read (bf16: 16x16x32 MFMAs) or one 4-byte read per 4-row step
+// (fp32: 16x16x4 MFMAs).  Wave w owns C rows 64*(w & 1) + [0,64) and columns
+// 64*(w >> 1) + [0,64): 4 x 4 tiles of 16 x 16.  Rows past the expert's count
+// stage as zeros.
+typedef float v4f_t __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf_t __attribute__((ext_vector_type(8)));
+constexpr int kWgTile = 128;
+constexpr int kWgRows = 32;
+constexpr int kWgStride = kWgRows + 8;       // LDS row stride in elements (padding vs bank conflicts)
+
+template <typename TE>
+__global__ __launch_bounds__(kThreads) void wgrad_kernel(const TE* __restrict__ b, const TE* __restrict__ a,
+                                                        const int32_t* __restrict__ counts,
+                                                        const int32_t* __restrict__ offsets, int64_t rows_cap,
+                                                        int N, int K, float* __restrict__ c) {
+  constexpr bool kF32 = sizeof(TE) == 4;
+  __shared__ __attribute__((aligned(16))) TE sB[kWgTile * kWgStride];
+  __shared__ __attribute__((aligned(16))) TE sA[kWgTile * kWgStride];
+  const int e = blockIdx.z;
+  const int n0 = blockIdx.y * kWgTile, k0 = blockIdx.x * kWgTile;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t off = offsets[e];
+  int cnt = 0;
+  if (off >= 0 && off < rows_cap) cnt = static_cast<int>(min<int64_t>(counts[e], rows_cap - off));
+  // staging: thread t moves rows 2*(t / 16) and 2*(t / 16) + 1, columns 8*(t % 16) + [0,8)
+  const int sr = 2 * (tid >> 4), sc = 8 * (tid & 15);
+  v4f_t acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = v4f_t{0.f, 0.f, 0.f, 0.f};
+  const int wn = 64 * (wave & 1), wk = 64 * (wave >> 1);
+  for (int r0 = 0; r0 < cnt; r0 += kWgRows) {
+    // 8 elements = 16 B (bf16) or 32 B (fp32) per row and operand
+    constexpr int kVec = kF32 ? 2 : 1;
+    uint4 vb[2][kVec], va[2][kVec];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int r = r0 + sr + h;
+      const bool live = r < cnt;
+      const uint4* brow = reinterpret_cast<const uint4*>(b + (off + r) * static_cast<int64_t>(N) + n0 + sc);
+      const uint4* arow = reinterpret_cast<const uint4*>(a + (off + r) * static_cast<int64_t>(K) + k0 + sc);
+#pragma unroll
+      for (int v = 0; v < kVec; ++v) {
+        vb[h][v] = live ? brow[v] : make_uint4(0, 0, 0, 0);
+        va[h][v] = live ? arow[v] : make_uint4(0, 0, 0, 0);
+      }
+    }
+    __syncthreads();                               // the previous chunk's reads are done
+    // rows sr and sr + 1 of one column are adjacent in LDS: one 4-byte (bf16)
+    // or 8-byte (fp32) write per column and operand
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if constexpr (kF32) {
+        const uint32_t* b0 = reinterpret_cast<const uint32_t*>(&vb[0][0]);
+        const uint32_t* b1 = reinterpret_cast<const uint32_t*>(&vb[1][0]);
+        const uint32_t* a0 = reinterpret_cast<const uint32_t*>(&va[0][0]);
+        const uint32_t* a1 = reinterpret_cast<const uint32_t*>(&va[1][0]);
+        *reinterpret_cast<uint2*>(&sB[(sc + i) * kWgStride + sr]) = make_uint2(b0[i], b1[i]);
+        *reinterpret_cast<uint2*>(&sA[(sc + i) * kWgStride + sr]) = make_uint2(a0[i], a1[i]);
+      } else {
+        const uint16_t* b0 = reinterpret_cast<const uint16_t*>(&vb[0][0]);
+        const uint16_t* b1 = reinterpret_cast<const uint16_t*>(&vb[1][0]);
+        const uint16_t* a0 = reinterpret_cast<const uint16_t*>(&va[0][0]);
+        const uint16_t* a1 = reinterpret_cast<const uint16_t*>(&va[1][0]);
+        *reinterpret_cast<uint32_t*>(&sB[(sc + i) * kWgStride + sr]) = b0[i] | (uint32_t(b1[i]) << 16);
+        *reinterpret_cast<uint32_t*>(&sA[(sc + i) * kWgStride + sr]) = a0[i] | (uint32_t(a1[i]) << 16);
+      }
+    }
+    __syncthreads();
+    if constexpr (!kF32) {
+      v8bf_t fb[4], fa[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        fb[i] = *reinterpret_cast<const v8bf_t*>(&sB[(wn + 16 * i + (lane & 15)) * kWgStride + 8 * (lane >> 4)]);
+        fa[i] = *reinterpret_cast<const v8bf_t*>(&sA[(wk + 16 * i + (lane & 15)) * kWgStride + 8 * (lane >> 4)]);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[i], fa[j], acc[i][j], 0, 0, 0);
+    } else {
+#pragma unroll
+      for (int s = 0; s < kWgRows / 4; ++s) {
+        float fb[4], fa[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          fb[i] = reinterpret_cast<const float*>(sB)[(wn + 16 * i + (lane & 15)) * kWgStride + 4 * s + (lane >> 4)];
+          fa[i] = reinterpret_cast<const float*>(sA)[(wk + 16 * i + (lane & 15)) * kWgStride + 4 * s + (lane >> 4)];
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(fb[i], fa[j], acc[i][j], 0, 0, 0);
+      }
+    }
+  }
+  // lane holds C[n = 16i + 4*(lane >> 4) + r][k = 16j + (lane & 15)] of the wave's 64 x 64
+  float* ce = c + static_cast<int64_t>(e) * N * K;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int n = n0 + wn + 16 * i + 4 * (lane >> 4) + r;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) ce[static_cast<int64_t>(n) * K + k0 + wk + 16 * j + (lane & 15)] = acc[i][j][r];
+    }
+}
+
 }  // namespace
+
+extern "C" moe_status moe_grouped_gemm_wgrad(const void* b, const void* a, moe_dtype dt,
+                                             const int32_t* counts, const int32_t* offsets, int L,
+                                             int64_t rows_cap, int N, int K, float* c, hipStream_t stream) {
+  MOE_CHECK(L >= 1 && L <= 65535 && rows_cap >= 0 && N > 0 && K > 0 && moe_host::valid_dtype(dt),
+            MOE_ERR_INVALID_ARG);
+  MOE_CHECK(dt != MOE_FP8_E4M3, MOE_ERR_UNSUPPORTED);
+  MOE_CHECK(N % kWgTile == 0 && K % kWgTile == 0, MOE_ERR_UNSUPPORTED);
+  MOE_CHECK(c && counts && offsets && (rows_cap == 0 || (a && b)), MOE_ERR_INVALID_ARG);
+  MOE_CHECK(((reinterpret_cast<uintptr_t>(a) | reinterpret_cast<uintptr_t>(b)) & 15) == 0, MOE_ERR_INVALID_ARG);
+  const dim3 grid(K / kWgTile, N / kWgTile, L);
+  if (dt == MOE_F32)
+    wgrad_kernel<float><<<grid, kThreads, 0, stream>>>(static_cast<const float*>(b), static_cast<const float*>(a),
+                                                       counts, offsets, rows_cap, N, K, c);
+  else
+    wgrad_kernel<__bf16><<<grid, kThreads, 0, stream>>>(static_cast<const __bf16*>(b), static_cast<const __bf16*>(a),
+                                                        counts, offsets, rows_cap, N, K, c);
+  MOE_LAUNCH_CHECK();
+  return MOE_OK;
+}
 
 extern "C" moe_status moe_combine_backward(const void* dy, moe_dtype dy_dt, const void* expert_out,
                                            moe_dtype eo_dt, const int32_t* slot_of,

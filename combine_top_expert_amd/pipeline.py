@@ -20,7 +20,7 @@ from . import (MOE_EPI_SILU_MUL, MOE_EPI_STORE_G, moe_combine, moe_dispatch_layo
                moe_dispatch_layout_workspace_bytes, moe_grouped_gemm_w2, moe_grouped_gemm_w13,
                moe_grouped_gemm_workspace_bytes, moe_pack_w13, MOE_W_PACKED, MOE_W_ROW_MAJOR,
                moe_combine_backward, moe_silu_mul_backward, moe_permute_backward,
-               moe_transpose_weights,
+               moe_transpose_weights, moe_grouped_gemm_wgrad,
                moe_permute, moe_silu_mul)
 
 _TORCH = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8}
@@ -154,24 +154,49 @@ class MoELayer:
             self.dg = torch.empty(rc, 2 * s.I, dtype=gdt, device=dev)
             self.da = torch.empty(rc, s.H, dtype=gdt, device=dev)
             self.dx = torch.empty(s.T, s.H, dtype=gdt, device=dev)
+            self.dw2 = torch.empty(s.L, s.H, s.I, dtype=torch.float32, device=dev)
+            self.dw13 = torch.empty(s.L, 2 * s.I, s.H, dtype=torch.float32, device=dev)
 
-    def backward(self, dy, topk_weights):
-        """Gradients of the last forward for dy [T,H]: returns (dx [T,H],
-        d_w [T,K]).  Reuses the forward's routing (slot_of, counts, offsets),
-        its permuted activations and expert outputs; G is recomputed."""
+    def backward_stages(self, dy, topk_weights, weight_grads=True):
+        """The backward as (name, launch) pairs in run order, for dy [T,H]:
+        combine backward, dZ = d_out W2 (on W2^T), G recomputed, SiLU*up
+        backward, dA = dG W13 (on W13^T), permute backward, then with
+        weight_grads dW2 = d_out^T Z and dW13 = dG^T A per expert."""
         self.prepare_backward()
-        moe_combine_backward(dy, self.out, self.slot_of, topk_weights, self.d_out, self.d_w)
-        moe_grouped_gemm_w2(self.d_out, None, self.w2_t, None, self.counts, self.offsets, self.dz,
-                            workspace=self.gemm_workspace)
         w, lay = ((self.w13_packed, MOE_W_PACKED) if self.w13_packed is not None
                   else (self.w13, MOE_W_ROW_MAJOR))
-        moe_grouped_gemm_w13(self.buf, self.buf_scales, w, self.w13_scales, self.counts,
-                             self.offsets, MOE_EPI_STORE_G, self.g_saved,
-                             workspace=self.gemm_workspace, w13_layout=lay)
-        moe_silu_mul_backward(self.g_saved, self.dz, self.counts, self.offsets, self.dg)
-        moe_grouped_gemm_w2(self.dg, None, self.w13_t, None, self.counts, self.offsets, self.da,
-                            workspace=self.gemm_workspace)
-        moe_permute_backward(self.da, self.slot_of, self.dx)
+        st = [
+            ("combine_bw", lambda: moe_combine_backward(dy, self.out, self.slot_of, topk_weights,
+                                                        self.d_out, self.d_w)),
+            ("gemm_dz", lambda: moe_grouped_gemm_w2(self.d_out, None, self.w2_t, None, self.counts,
+                                                    self.offsets, self.dz, workspace=self.gemm_workspace)),
+            ("gemm_g", lambda: moe_grouped_gemm_w13(self.buf, self.buf_scales, w, self.w13_scales,
+                                                    self.counts, self.offsets, MOE_EPI_STORE_G,
+                                                    self.g_saved, workspace=self.gemm_workspace,
+                                                    w13_layout=lay)),
+            ("silu_mul_bw", lambda: moe_silu_mul_backward(self.g_saved, self.dz, self.counts,
+                                                          self.offsets, self.dg)),
+            ("gemm_da", lambda: moe_grouped_gemm_w2(self.dg, None, self.w13_t, None, self.counts,
+                                                    self.offsets, self.da, workspace=self.gemm_workspace)),
+            ("permute_bw", lambda: moe_permute_backward(self.da, self.slot_of, self.dx)),
+        ]
+        if weight_grads:
+            st += [
+                ("wgrad_w2", lambda: moe_grouped_gemm_wgrad(self.d_out, self.z, self.counts,
+                                                            self.offsets, self.dw2)),
+                ("wgrad_w13", lambda: moe_grouped_gemm_wgrad(self.dg, self.buf, self.counts,
+                                                             self.offsets, self.dw13)),
+            ]
+        return st
+
+    def backward(self, dy, topk_weights, weight_grads=True):
+        """Gradients of the last forward for dy [T,H]: returns (dx [T,H],
+        d_w [T,K]); with weight_grads also fills dw2 [L,H,I] = d_out^T Z and
+        dw13 [L,2I,H] = dG^T A per expert.  Reuses the forward's routing
+        (slot_of, counts, offsets), its permuted activations, Z and expert
+        outputs; G is recomputed."""
+        for _, f in self.backward_stages(dy, topk_weights, weight_grads):
+            f()
         return self.dx, self.d_w
 
     def forward(self, x, topk_ids, topk_weights):

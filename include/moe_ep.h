@@ -81,7 +81,7 @@ const char* moe_status_string(int status);
 
 /* ABI version; bumped on any signature change or added entry point (2: moe_router_topk;
  * 3: GEMM workspace for the K-split last round; 4: moe_pack_w13 and the W13 layout;
- * 5: the backward entry points). */
+ * 5: the backward entry points; 6: moe_grouped_gemm_wgrad). */
 int moe_abi_version(void);
 
 /* Bytes of device workspace moe_dispatch_layout needs for (T, K, L). */
@@ -296,6 +296,8 @@ moe_status moe_router_topk(const float* logits, const float* bias, int T, int E,
  *   dG    = silu_mul_backward(G, dZ)        moe_silu_mul_backward
  *   dA    = dG W13[e]                       moe_grouped_gemm_w2 on W13^T [L,H,2I]
  *   dx    = permute_backward(dA)            moe_permute_backward
+ *   dW2   = d_out^T Z   per expert          moe_grouped_gemm_wgrad
+ *   dW13  = dG^T A      per expert          moe_grouped_gemm_wgrad
  *
  * moe_grouped_gemm_w2 computes rows * W^T for any [L, N, K] weights (N = its
  * H argument, K = its I argument), so with the transposes written once by
@@ -347,6 +349,22 @@ moe_status moe_permute_backward(const void* d_buf, moe_dtype d_buf_dt, const int
  */
 moe_status moe_transpose_weights(const void* w, moe_dtype w_dt, int L, int N, int K, void* wt,
                                  hipStream_t stream);
+
+/*
+ * moe_grouped_gemm_wgrad -- weight gradient of a grouped GEMM: for every local
+ * expert e, C[e] = sum over its valid rows q of b[q]^T a[q] (an outer-product
+ * sum, fp32 accumulation), i.e. dW2[e] = d_out^T Z (b = d_out, a = Z) and
+ * dW13[e] = dG^T A (b = dG, a = the permuted buffer).  Rows are expert e's
+ * [offsets[e], offsets[e] + counts[e]) (clamped to rows_cap); padding rows
+ * are never read.  An expert without rows gets C[e] = 0.
+ *   b [rows_cap,N], a [rows_cap,K] (dt, row-major, 16-byte aligned),
+ *   c [L,N,K] fp32, caller-owned, every element written.
+ * dtypes: F32 or BF16 (FP8 buffers: MOE_ERR_UNSUPPORTED).
+ * Limits: N % 128 == 0, K % 128 == 0, L <= 65535.
+ */
+moe_status moe_grouped_gemm_wgrad(const void* b, const void* a, moe_dtype dt, const int32_t* counts,
+                                  const int32_t* offsets, int L, int64_t rows_cap, int N, int K,
+                                  float* c, hipStream_t stream);
 
 #ifdef __cplusplus
 }

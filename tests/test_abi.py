@@ -36,9 +36,10 @@ def test_header_declares_the_entry_points():
     for name in ["moe_dispatch_layout", "moe_permute", "moe_grouped_gemm_w13", "moe_silu_mul",
                  "moe_grouped_gemm_w2", "moe_combine", "moe_router_topk",
                  "moe_grouped_gemm_workspace_bytes", "moe_pack_w13", "moe_combine_backward",
-                 "moe_silu_mul_backward", "moe_permute_backward", "moe_transpose_weights"]:
+                 "moe_silu_mul_backward", "moe_permute_backward", "moe_transpose_weights",
+                 "moe_grouped_gemm_wgrad"]:
         assert name in fns
-    assert len(fns) == 16
+    assert len(fns) == 17
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -57,7 +58,7 @@ def test_status_strings_and_version(lib):
     assert lib.moe_status_string(0) == b"MOE_OK"
     assert lib.moe_status_string(-2) == b"MOE_ERR_UNSUPPORTED"
     assert lib.moe_status_string(12345) == b"MOE_ERR_UNKNOWN"
-    assert lib.moe_abi_version() == 5
+    assert lib.moe_abi_version() == 6
 
 
 def test_workspace_bytes(lib):
@@ -178,7 +179,7 @@ def test_python_binding_loads_and_matches_header(lib):
     import combine_top_expert_amd as ep
     for name in declared_functions():
         assert callable(getattr(ep, name)), name
-    assert ep.moe_abi_version() == 5
+    assert ep.moe_abi_version() == 6
     assert ep.moe_status_string(-1) == "MOE_ERR_INVALID_ARG"
 
 
@@ -241,3 +242,16 @@ def test_backward_argument_errors(lib):
     assert tw(P(), 2, 2, 128, 128, P(8), None) == UNSUPPORTED                            # fp8
     assert tw(P(), 1, 2, 128, 128, P(), None) == INVALID                                 # in place
     assert tw(P(), 1, 0, 128, 128, P(8), None) == INVALID
+    wg = lib.moe_grouped_gemm_wgrad
+    wg.restype = ctypes.c_int
+    wg.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                   ctypes.c_int, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                   ctypes.c_void_p]
+    A = P(256)
+    assert wg(A, A, 2, A, A, 4, 64, 128, 128, A, None) == UNSUPPORTED                   # fp8
+    assert wg(A, A, 1, A, A, 4, 64, 192, 128, A, None) == UNSUPPORTED                   # N % 128
+    assert wg(A, A, 1, A, A, 4, 64, 128, 96, A, None) == UNSUPPORTED                    # K % 128
+    assert wg(A, A, 1, A, A, 0, 64, 128, 128, A, None) == INVALID                       # L = 0
+    assert wg(A, A, 1, A, A, 4, 64, 128, 128, None, None) == INVALID                    # no c
+    assert wg(P(258), A, 1, A, A, 4, 64, 128, 128, A, None) == INVALID                  # misaligned b
+    assert wg(A, None, 1, A, A, 4, 64, 128, 128, A, None) == INVALID                    # no a

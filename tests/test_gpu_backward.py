@@ -11,8 +11,11 @@ oracle's step on the same values:
   * SiLU*up backward: hardware exp2/reciprocal against numpy's exp, 1e-5
     relative L2 (fp32) or the bf16 step;
   * permute backward: bit-exact (fp32 sums in k order);
-and end to end, dx and d_w against the oracle's own backward (its own
-forward values), to the bars the rounding chain allows."""
+  * weight gradients dW2 = d_out^T Z and dW13 = dG^T A: fp32 sums of exact
+    products against float64, 1e-5 relative L2 per expert, exact zeros for
+    experts without rows;
+and end to end, dx, d_w, dW2 and dW13 against the oracle's own backward (its
+own forward values), to the bars the rounding chain allows."""
 import numpy as np
 import pytest
 import torch
@@ -98,6 +101,17 @@ def test_backward_stages(ep, name):
     dx_ref = B.permute_backward({int(q): da[q] for q in rows}, slot_of, cfg.H, gdt)
     dx = host_vals(layer.dx)
     assert np.array_equal(dx.view(np.uint32), dx_ref.view(np.uint32))
+    # weight gradients on the GPU's own d_out, Z, dG and A
+    z, a = host_vals(layer.z), host_vals(layer.buf)
+    dw2, dw13 = layer.dw2.cpu().numpy(), layer.dw13.cpu().numpy()
+    for e in range(cfg.L):
+        qs = [q for q in rows if e_of[int(q)] == e]
+        for got, bb, aa in ((dw2[e], d_out, z), (dw13[e], dg, a)):
+            ref = B.wgrad(bb[qs], aa[qs], got.shape[0], got.shape[1])
+            if not qs:
+                assert not np.any(got)
+            else:
+                assert rel_l2(got, ref) < 1e-5, (e, len(qs))
     print(f"[metric] backward {name}: d_w rel {rel_l2(d_w, d_w_ref):.1e}", flush=True)
 
 
@@ -111,6 +125,9 @@ def test_backward_end_to_end(ep, name):
     print(f"[metric] backward e2e {name}: dx rel_l2 {ex:.2e}, d_w rel_l2 {ew_:.2e}", flush=True)
     bar = 1e-5 if cfg.act == "f32" else 2e-2
     assert ex < bar and ew_ < bar
+    e2, e13 = rel_l2(layer.dw2.cpu().numpy(), res["dw2"]), rel_l2(layer.dw13.cpu().numpy(), res["dw13"])
+    print(f"[metric] backward e2e {name}: dW2 rel_l2 {e2:.2e}, dW13 rel_l2 {e13:.2e}", flush=True)
+    assert e2 < bar and e13 < bar
     no_local = ~(layer.slot_of.cpu().numpy() >= 0).any(axis=1)
     assert np.all(dx[no_local] == 0)
 
@@ -122,3 +139,37 @@ def test_transpose_weights(ep):
         ep.moe_transpose_weights(w, wt)
         torch.cuda.synchronize()
         assert torch.equal(wt.cpu(), w.cpu().transpose(1, 2))
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_wgrad_ragged_experts(ep, dt):
+    """Ragged expert row counts (0, 1, one chunk short, one chunk over, many
+    chunks), padding rows filled with NaN (never read), several tiles in both
+    output dimensions: against float64 per expert."""
+    announce("wgrad ragged", dt)
+    counts = np.array([0, 1, 31, 33, 100, 0, 257], np.int32)
+    R = 288                                   # capacity per expert; rows past the count are padding
+    offsets = (np.arange(len(counts)) * R).astype(np.int32)
+    rows_cap, N, K = R * len(counts), 256, 384
+    rng = np.random.default_rng(21)
+    b = np.full((rows_cap, N), np.nan, np.float32)
+    a = np.full((rows_cap, K), np.nan, np.float32)
+    for e, c in enumerate(counts):
+        b[offsets[e]:offsets[e] + c] = rng.standard_normal((c, N))
+        a[offsets[e]:offsets[e] + c] = rng.standard_normal((c, K))
+    if dt == "bf16":
+        b, a = B.to_format(b, "bf16"), B.to_format(a, "bf16")
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    c_dev = torch.full((len(counts), N, K), 7.0, device="cuda")
+    ep.moe_grouped_gemm_wgrad(torch.from_numpy(b).cuda().to(tdt), torch.from_numpy(a).cuda().to(tdt),
+                              dev(counts), dev(offsets), c_dev)
+    torch.cuda.synchronize()
+    got = c_dev.cpu().numpy()
+    assert np.isfinite(got).all()
+    for e, c in enumerate(counts):
+        rs = slice(offsets[e], offsets[e] + c)
+        ref = B.wgrad(b[rs], a[rs], N, K)
+        if c == 0:
+            assert not np.any(got[e])
+        else:
+            assert rel_l2(got[e], ref) < 1e-5, (e, c, rel_l2(got[e], ref))
