@@ -183,28 +183,27 @@ __global__ __launch_bounds__(kThreads) void transpose_kernel(const TE* __restric
 
 // ---------------------------------------------------------------- weight gradients
 // C[e] = B_e^T A_e over expert e's valid rows: B [rows_cap, N], A [rows_cap, K]
-// -> C [L, N, K] fp32.  One workgroup per (expert, 128 x 128 tile of C);
-// rows are reduced in chunks of 32.  Each chunk of B (32 x 128) and A
-// (32 x 128) is staged into LDS transposed ([column][row], rows contiguous)
-// so that a matrix-core operand -- 8 consecutive rows of one column -- is one
-// 16-byte read (bf16: 16x16x32 MFMAs) or one 4-byte read per 4-row step
-// (fp32: 16x16x4 MFMAs).  Wave w owns C rows 64*(w & 1) + [0,64) and columns
-// 64*(w >> 1) + [0,64): 4 x 4 tiles of 16 x 16.  Rows past the expert's count
-// stage as zeros.
+// -> C [L, N, K] fp32.
+//
+// fp32 operands: one workgroup per (expert, 128 x 128 tile of C); rows are
+// reduced in chunks of 32.  Each chunk of B (32 x 128) and A (32 x 128) is
+// staged into LDS transposed ([column][row], rows contiguous) so that a
+// 16x16x4 matrix-core operand -- 4 consecutive rows of one column, one per
+// lane group -- is one 4-byte read per lane.  Wave w owns C rows
+// 64*(w & 1) + [0,64) and columns 64*(w >> 1) + [0,64): 4 x 4 tiles of
+// 16 x 16.  Rows past the expert's count stage as zeros.
 typedef float v4f_t __attribute__((ext_vector_type(4)));
 typedef __bf16 v8bf_t __attribute__((ext_vector_type(8)));
 constexpr int kWgTile = 128;
 constexpr int kWgRows = 32;
 constexpr int kWgStride = kWgRows + 8;       // LDS row stride in elements (padding vs bank conflicts)
 
-template <typename TE>
-__global__ __launch_bounds__(kThreads) void wgrad_kernel(const TE* __restrict__ b, const TE* __restrict__ a,
+__global__ __launch_bounds__(kThreads) void wgrad_f32_kernel(const float* __restrict__ b, const float* __restrict__ a,
                                                         const int32_t* __restrict__ counts,
                                                         const int32_t* __restrict__ offsets, int64_t rows_cap,
                                                         int N, int K, float* __restrict__ c) {
-  constexpr bool kF32 = sizeof(TE) == 4;
-  __shared__ __attribute__((aligned(16))) TE sB[kWgTile * kWgStride];
-  __shared__ __attribute__((aligned(16))) TE sA[kWgTile * kWgStride];
+  __shared__ __attribute__((aligned(16))) float sB[kWgTile * kWgStride];
+  __shared__ __attribute__((aligned(16))) float sA[kWgTile * kWgStride];
   const int e = blockIdx.z;
   const int n0 = blockIdx.y * kWgTile, k0 = blockIdx.x * kWgTile;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -220,8 +219,8 @@ __global__ __launch_bounds__(kThreads) void wgrad_kernel(const TE* __restrict__ 
     for (int j = 0; j < 4; ++j) acc[i][j] = v4f_t{0.f, 0.f, 0.f, 0.f};
   const int wn = 64 * (wave & 1), wk = 64 * (wave >> 1);
   for (int r0 = 0; r0 < cnt; r0 += kWgRows) {
-    // 8 elements = 16 B (bf16) or 32 B (fp32) per row and operand
-    constexpr int kVec = kF32 ? 2 : 1;
+    // 8 elements = 32 B per row and operand
+    constexpr int kVec = 2;
     uint4 vb[2][kVec], va[2][kVec];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -236,52 +235,30 @@ __global__ __launch_bounds__(kThreads) void wgrad_kernel(const TE* __restrict__ 
       }
     }
     __syncthreads();                               // the previous chunk's reads are done
-    // rows sr and sr + 1 of one column are adjacent in LDS: one 4-byte (bf16)
-    // or 8-byte (fp32) write per column and operand
+    // rows sr and sr + 1 of one column are adjacent in LDS: one 8-byte write
+    // per column and operand
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      if constexpr (kF32) {
-        const uint32_t* b0 = reinterpret_cast<const uint32_t*>(&vb[0][0]);
-        const uint32_t* b1 = reinterpret_cast<const uint32_t*>(&vb[1][0]);
-        const uint32_t* a0 = reinterpret_cast<const uint32_t*>(&va[0][0]);
-        const uint32_t* a1 = reinterpret_cast<const uint32_t*>(&va[1][0]);
-        *reinterpret_cast<uint2*>(&sB[(sc + i) * kWgStride + sr]) = make_uint2(b0[i], b1[i]);
-        *reinterpret_cast<uint2*>(&sA[(sc + i) * kWgStride + sr]) = make_uint2(a0[i], a1[i]);
-      } else {
-        const uint16_t* b0 = reinterpret_cast<const uint16_t*>(&vb[0][0]);
-        const uint16_t* b1 = reinterpret_cast<const uint16_t*>(&vb[1][0]);
-        const uint16_t* a0 = reinterpret_cast<const uint16_t*>(&va[0][0]);
-        const uint16_t* a1 = reinterpret_cast<const uint16_t*>(&va[1][0]);
-        *reinterpret_cast<uint32_t*>(&sB[(sc + i) * kWgStride + sr]) = b0[i] | (uint32_t(b1[i]) << 16);
-        *reinterpret_cast<uint32_t*>(&sA[(sc + i) * kWgStride + sr]) = a0[i] | (uint32_t(a1[i]) << 16);
-      }
+      const uint32_t* b0 = reinterpret_cast<const uint32_t*>(&vb[0][0]);
+      const uint32_t* b1 = reinterpret_cast<const uint32_t*>(&vb[1][0]);
+      const uint32_t* a0 = reinterpret_cast<const uint32_t*>(&va[0][0]);
+      const uint32_t* a1 = reinterpret_cast<const uint32_t*>(&va[1][0]);
+      *reinterpret_cast<uint2*>(&sB[(sc + i) * kWgStride + sr]) = make_uint2(b0[i], b1[i]);
+      *reinterpret_cast<uint2*>(&sA[(sc + i) * kWgStride + sr]) = make_uint2(a0[i], a1[i]);
     }
     __syncthreads();
-    if constexpr (!kF32) {
-      v8bf_t fb[4], fa[4];
+#pragma unroll
+    for (int s = 0; s < kWgRows / 4; ++s) {
+      float fb[4], fa[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        fb[i] = *reinterpret_cast<const v8bf_t*>(&sB[(wn + 16 * i + (lane & 15)) * kWgStride + 8 * (lane >> 4)]);
-        fa[i] = *reinterpret_cast<const v8bf_t*>(&sA[(wk + 16 * i + (lane & 15)) * kWgStride + 8 * (lane >> 4)]);
+        fb[i] = sB[(wn + 16 * i + (lane & 15)) * kWgStride + 4 * s + (lane >> 4)];
+        fa[i] = sA[(wk + 16 * i + (lane & 15)) * kWgStride + 4 * s + (lane >> 4)];
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[i], fa[j], acc[i][j], 0, 0, 0);
-    } else {
-#pragma unroll
-      for (int s = 0; s < kWgRows / 4; ++s) {
-        float fb[4], fa[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          fb[i] = reinterpret_cast<const float*>(sB)[(wn + 16 * i + (lane & 15)) * kWgStride + 4 * s + (lane >> 4)];
-          fa[i] = reinterpret_cast<const float*>(sA)[(wk + 16 * i + (lane & 15)) * kWgStride + 4 * s + (lane >> 4)];
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(fb[i], fa[j], acc[i][j], 0, 0, 0);
-      }
+        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(fb[i], fa[j], acc[i][j], 0, 0, 0);
     }
   }
   // lane holds C[n = 16i + 4*(lane >> 4) + r][k = 16j + (lane & 15)] of the wave's 64 x 64
@@ -293,6 +270,169 @@ __global__ __launch_bounds__(kThreads) void wgrad_kernel(const TE* __restrict__ 
       const int n = n0 + wn + 16 * i + 4 * (lane >> 4) + r;
 #pragma unroll
       for (int j = 0; j < 4; ++j) ce[static_cast<int64_t>(n) * K + k0 + wk + 16 * j + (lane & 15)] = acc[i][j][r];
+    }
+}
+
+constexpr int kW2Tile = 256;
+
+// bf16 weight gradients, staged by direct global-to-LDS loads.  A ring of
+// kW3Stages stages, each 32 rows x 256 columns of both operands in row-major
+// order (512 bytes per row, the layout in memory), keeps kW3Stages - 1 chunks
+// of loads in flight while one is multiplied.  Within a row the 16-byte chunk
+// c sits at position c ^ 2 * (row & 3), so that the four rows one transposed
+// read touches fall in four different 32-byte bank windows.  A matrix-core
+// operand (8 consecutive rows of one column) is two transposed LDS reads
+// (ds_read_b64_tr_b16: within 16 lanes, lane 4*d + q names row d, columns
+// 4q..4q+3, and lane j receives column j of those four rows).  Rows past the
+// expert's count read as zeros through the bound of a buffer resource made
+// per chunk (based at the chunk's first row, so offsets stay small for any
+// expert size).  Eight waves: wave w owns C rows 128*(w & 1) + [0,128) and
+// columns 64*(w >> 1) + [0,64) of the 256 x 256 tile (8 x 4 MFMA tiles, 128
+// accumulators), so two waves fit on a SIMD.  N and K need only be multiples
+// of 128: columns past them stage garbage that only the waves owning those
+// columns would read, and those waves skip both the products and the stores.
+// Blocks are numbered expert-major, then n tile, then k tile.
+constexpr int kW3Threads = 512;
+constexpr int kW3Rows = 32;
+constexpr int kW3Stages = 4;
+constexpr int kW3OpBytes = kW3Rows * kW2Tile * 2;       // one operand of one stage: 16 KB
+constexpr int kW3StageBytes = 2 * kW3OpBytes;
+constexpr int kW3LoadsPerChunk = 4;                     // per thread: 2 per operand
+constexpr uint32_t kW3RsrcWord3 = 0x00020000u;
+
+template <int N> struct W3VmCnt {
+  static constexpr int imm = (N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8);
+};
+
+typedef short v4s_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4s_t* lds_v4s_t;
+typedef __attribute__((address_space(3))) void* lds_void_t;
+
+// byte offset, within one operand of a stage, of this lane's first transposed
+// read for the 16 columns starting at col0 (the second read is 4 rows = 2048
+// bytes further)
+__device__ __forceinline__ int tr_offset(int col0, int lane) {
+  const int g = lane >> 4, d = (lane >> 2) & 3, q = lane & 3;
+  const int c = (col0 >> 3) + (q >> 1);                 // logical 16-byte chunk
+  return (8 * g + d) * 512 + ((c ^ (2 * d)) << 4) + ((q & 1) << 3);
+}
+
+// Transposed reads are written as inline assembly: as compiler builtins they
+// would make the compiler wait for every outstanding global-to-LDS load (it
+// cannot tell that they target other stages).  Their results are used only
+// after lds_wait() below, which passes them through an explicit lgkmcnt wait.
+typedef int v2i_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ v8bf_t tr_fragment(uint32_t addr) {
+  v2i_t lo, hi;
+  asm volatile("ds_read_b64_tr_b16 %0, %2\n\tds_read_b64_tr_b16 %1, %2 offset:2048"
+               : "=v"(lo), "=v"(hi)
+               : "v"(addr));
+  const v2i_t both[2] = {lo, hi};
+  return *reinterpret_cast<const v8bf_t*>(both);
+}
+
+__device__ __forceinline__ void lds_wait(v8bf_t (&f)[4]) {
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(f[0]), "+v"(f[1]), "+v"(f[2]), "+v"(f[3]));
+}
+
+__global__ __launch_bounds__(kW3Threads, 1) void wgrad_bf16_lds_kernel(
+    const uint16_t* __restrict__ b, const uint16_t* __restrict__ a, const int32_t* __restrict__ counts,
+    const int32_t* __restrict__ offsets, int64_t rows_cap, int N, int K, int tiles_n, int tiles_k,
+    float* __restrict__ c) {
+  __shared__ __attribute__((aligned(16))) uint8_t s_ring[kW3Stages * kW3StageBytes];
+  const int per_e = tiles_n * tiles_k;
+  const int e = blockIdx.x / per_e;
+  const int rem = blockIdx.x - e * per_e;
+  const int n0 = (rem / tiles_k) * kW2Tile, k0 = (rem % tiles_k) * kW2Tile;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t off = offsets[e];
+  int cnt = 0;
+  if (off >= 0 && off < rows_cap) cnt = static_cast<int>(min<int64_t>(counts[e], rows_cap - off));
+  const int wn = 128 * (wave & 1), wk = 64 * (wave >> 1);
+  const bool active = n0 + wn < N && k0 + wk < K;
+  // load j of this wave covers rows 4*wave + 2j + [0,2) of a chunk: the
+  // lane's row is 4*wave + 2j + (lane >> 5), its chunk position lane & 31
+  int vB[2], vA[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int row = 4 * wave + 2 * j + (lane >> 5);
+    const int cl = (lane & 31) ^ (2 * (row & 3));
+    vB[j] = row * N * 2 + n0 * 2 + cl * 16;
+    vA[j] = row * K * 2 + k0 * 2 + cl * 16;
+  }
+  auto issue = [&](int chunk) {
+    uint8_t* st = s_ring + (chunk % kW3Stages) * kW3StageBytes;
+    const int r0 = chunk * kW3Rows;
+    const int rows = min(kW3Rows, cnt - r0);            // reads of rows past the count return 0
+    const __amdgpu_buffer_rsrc_t rB = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(b + (off + r0) * N), 0, rows * N * 2, kW3RsrcWord3);
+    const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(a + (off + r0) * K), 0, rows * K * 2, kW3RsrcWord3);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, (lds_void_t)(st + (4 * wave + 2 * j) * 512), 16, vB[j], 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_void_t)(st + kW3OpBytes + (4 * wave + 2 * j) * 512), 16,
+                                               vA[j], 0, 0, 0);
+    }
+  };
+  const uint32_t lds_ring = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void_t)s_ring));
+  uint32_t ob[8], oa[4];
+#pragma unroll
+  for (int x = 0; x < 8; ++x) ob[x] = tr_offset(wn + 16 * x, lane);
+#pragma unroll
+  for (int y = 0; y < 4; ++y) oa[y] = kW3OpBytes + tr_offset(wk + 16 * y, lane);
+  v4f_t acc[8][4];
+#pragma unroll
+  for (int x = 0; x < 8; ++x)
+#pragma unroll
+    for (int y = 0; y < 4; ++y) acc[x][y] = v4f_t{0.f, 0.f, 0.f, 0.f};
+  const int nchunks = (cnt + kW3Rows - 1) / kW3Rows;
+  for (int ch = 0; ch < kW3Stages - 1 && ch < nchunks; ++ch) issue(ch);
+  for (int i = 0; i < nchunks; ++i) {
+    // this thread's loads of chunk i have landed once at most the loads of
+    // the chunks issued after it are outstanding
+    const int after = min(kW3Stages - 2, nchunks - 1 - i);
+    if (after >= 2) __builtin_amdgcn_s_waitcnt(W3VmCnt<2 * kW3LoadsPerChunk>::imm);
+    else if (after == 1) __builtin_amdgcn_s_waitcnt(W3VmCnt<kW3LoadsPerChunk>::imm);
+    else __builtin_amdgcn_s_waitcnt(W3VmCnt<0>::imm);
+    // chunk i visible; chunk i - 1 fully read (its reads completed before its
+    // products).  A bare barrier: no fence, which would wait for every load.
+    asm volatile("s_barrier" ::: "memory");
+    if (i + kW3Stages - 1 < nchunks) issue(i + kW3Stages - 1);
+    if (active) {
+      const uint32_t st = lds_ring + (i % kW3Stages) * kW3StageBytes;
+      v8bf_t fa[4], fb0[4], fb1[4];
+#pragma unroll
+      for (int y = 0; y < 4; ++y) fa[y] = tr_fragment(st + oa[y]);
+#pragma unroll
+      for (int x = 0; x < 4; ++x) fb0[x] = tr_fragment(st + ob[x]);
+      lds_wait(fa);
+      lds_wait(fb0);
+#pragma unroll
+      for (int x = 0; x < 4; ++x) fb1[x] = tr_fragment(st + ob[4 + x]);
+#pragma unroll
+      for (int x = 0; x < 4; ++x)
+#pragma unroll
+        for (int y = 0; y < 4; ++y)
+          acc[x][y] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb0[x], fa[y], acc[x][y], 0, 0, 0);
+      lds_wait(fb1);
+#pragma unroll
+      for (int x = 0; x < 4; ++x)
+#pragma unroll
+        for (int y = 0; y < 4; ++y)
+          acc[4 + x][y] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb1[x], fa[y], acc[4 + x][y], 0, 0, 0);
+    }
+  }
+  if (!active) return;
+  float* ce = c + static_cast<int64_t>(e) * N * K;
+#pragma unroll
+  for (int x = 0; x < 8; ++x)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int n = n0 + wn + 16 * x + 4 * (lane >> 4) + r;
+#pragma unroll
+      for (int y = 0; y < 4; ++y)
+        __builtin_nontemporal_store(acc[x][y][r], &ce[static_cast<int64_t>(n) * K + k0 + wk + 16 * y + (lane & 15)]);
     }
 }
 
@@ -309,11 +449,16 @@ extern "C" moe_status moe_grouped_gemm_wgrad(const void* b, const void* a, moe_d
   MOE_CHECK(((reinterpret_cast<uintptr_t>(a) | reinterpret_cast<uintptr_t>(b)) & 15) == 0, MOE_ERR_INVALID_ARG);
   const dim3 grid(K / kWgTile, N / kWgTile, L);
   if (dt == MOE_F32)
-    wgrad_kernel<float><<<grid, kThreads, 0, stream>>>(static_cast<const float*>(b), static_cast<const float*>(a),
+    wgrad_f32_kernel<<<grid, kThreads, 0, stream>>>(static_cast<const float*>(b), static_cast<const float*>(a),
                                                        counts, offsets, rows_cap, N, K, c);
-  else
-    wgrad_kernel<__bf16><<<grid, kThreads, 0, stream>>>(static_cast<const __bf16*>(b), static_cast<const __bf16*>(a),
-                                                        counts, offsets, rows_cap, N, K, c);
+  else {
+    const int tn = (N + kW2Tile - 1) / kW2Tile, tk = (K + kW2Tile - 1) / kW2Tile;
+    const int64_t blocks = static_cast<int64_t>(L) * tn * tk;
+    MOE_CHECK(blocks <= INT32_MAX, MOE_ERR_UNSUPPORTED);
+    MOE_CHECK(32LL * std::max(N, K) * 2 < (int64_t(1) << 31), MOE_ERR_UNSUPPORTED);   // per-chunk offsets
+    wgrad_bf16_lds_kernel<<<static_cast<unsigned>(blocks), kW3Threads, 0, stream>>>(
+        static_cast<const uint16_t*>(b), static_cast<const uint16_t*>(a), counts, offsets, rows_cap, N, K, tn, tk, c);
+  }
   MOE_LAUNCH_CHECK();
   return MOE_OK;
 }
