@@ -151,32 +151,54 @@ def router_timing(cfg, steps, dev):
             "shape": {"T": cfg.T, "E": cfg.E, "K": cfg.K, "bias": cfg.bias}}
 
 
-def backward_timing(cfg, layer, w, steps, dev):
-    """The layer's backward (bf16 / fp32 weights) after the timed forward:
-    each stage timed with events around it over ``steps`` passes (medians).
-    GEMM stages report TFLOP/s, streaming stages GB/s of algorithmic bytes."""
+def _time_stages(stages, steps, dev):
+    """Median microseconds of each (name, launch) stage over ``steps`` passes,
+    an event between stages, and the median of the pass totals."""
+    import torch
+
+    for _ in range(3):
+        for _, f in stages:
+            f()
+    stream = torch.cuda.current_stream(dev)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for s in range(steps):
+        ev[s][0].record(stream)
+        for i, (_, f) in enumerate(stages):
+            f()
+            ev[s][i + 1].record(stream)
+    torch.cuda.synchronize()
+    per = np.array([[ev[s][i].elapsed_time(ev[s][i + 1]) for i in range(len(stages))]
+                    for s in range(steps)]) * 1e3
+    return ({name: float(np.median(per[:, i])) for i, (name, _) in enumerate(stages)},
+            float(np.median(per.sum(axis=1))))
+
+
+def backward_timing(cfg, layer, x, ids, w, steps, dev):
+    """The layer's backward (bf16 / fp32 weights), each stage timed with
+    events around it over ``steps`` passes (medians), in two settings:
+    after the fused forward (the backward recomputes G), and after the
+    unfused forward, which stores fp32 G (gate/up GEMM + SiLU*up, also timed)
+    so the backward skips the recompute.  GEMM stages report TFLOP/s,
+    streaming stages GB/s of algorithmic bytes."""
     import torch
 
     g = torch.Generator(device=dev)
     g.manual_seed(cfg.seed + 17)
     gb = {"bf16": 2, "f32": 4}[cfg.out_dt]
     dy = torch.randn(cfg.T, cfg.H, device=dev, generator=g).to(layer.out.dtype)
-    st = layer.backward_stages(dy, w)
-    for _ in range(3):
-        for _, f in st:
-            f()
-    stream = torch.cuda.current_stream(dev)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(st) + 1)] for _ in range(steps)]
-    torch.cuda.synchronize()
-    for s in range(steps):
-        ev[s][0].record(stream)
-        for i, (_, f) in enumerate(st):
-            f()
-            ev[s][i + 1].record(stream)
-    torch.cuda.synchronize()
-    per = np.array([[ev[s][i].elapsed_time(ev[s][i + 1]) for i in range(len(st))]
-                    for s in range(steps)]) * 1e3                     # us
-    us = {name: float(np.median(per[:, i])) for i, (name, _) in enumerate(st)}
+    layer.forward(x, ids, w)
+    us, total = _time_stages(layer.backward_stages(dy, w), steps, dev)
+    # unfused forward keeping G, then the backward without the recompute
+    layer.set_fused(False)
+    layer.forward(x, ids, w)
+    fwd_us, _ = _time_stages([("gemm_w13_store_g", layer.gemm_w13), ("silu_mul", layer.silu_mul)],
+                             steps, dev)
+    layer.forward(x, ids, w)
+    us_saved, total_saved = _time_stages(layer.backward_stages(dy, w), steps, dev)
+    layer.set_fused(True)
+    layer.forward(x, ids, w)
+
     rows = int(layer.counts.cpu().numpy().sum())
     T, K, H, I = cfg.T, cfg.K, cfg.H, cfg.I
     tok_local = int((layer.slot_of.cpu().numpy() >= 0).any(axis=1).sum())
@@ -191,10 +213,15 @@ def backward_timing(cfg, layer, w, steps, dev):
         "permute_bw": rows * H * gb + T * H * gb + T * K * 4,
     }
     peak = MFMA_PEAK_TFLOPS[cfg.wdt]
-    res = {"us": us, "total_us": float(np.median(per.sum(axis=1))), "rows": rows,
-           "timing": "medians over the passes, an event between stages",
+    res = {"us": us, "total_us": total, "rows": rows,
+           "timing": "medians over the passes, an event between stages; after the fused forward "
+                     "(G recomputed)",
            "tflops": {k: v / (us[k] * 1e-6) / 1e12 for k, v in flops.items()},
-           "gbs": {k: v / (us[k] * 1e-6) / 1e9 for k, v in nbytes.items()}}
+           "gbs": {k: v / (us[k] * 1e-6) / 1e9 for k, v in nbytes.items()},
+           "saved_g": {"backward_us": us_saved, "backward_total_us": total_saved,
+                       "forward_unfused_us": fwd_us,
+                       "note": "unfused forward (gate/up GEMM storing fp32 G, then SiLU*up) keeps G; "
+                               "the backward then skips the recompute"}}
     res["mfma_frac"] = {k: v / peak for k, v in res["tflops"].items()}
     res["hbm_frac"] = {k: v / HBM_PEAK_GBS for k, v in res["gbs"].items()}
     return res
@@ -361,7 +388,7 @@ def main():
         out["next_rows"]["router_topk"] = router_timing(cfg, args.steps, dev)
     if cfg.wdt != "fp8" and not args.skip_backward:
         print("[bench] backward stages", file=sys.stderr, flush=True)
-        out["next_rows"]["backward"] = backward_timing(cfg, layer, w, min(args.steps, 20), dev)
+        out["next_rows"]["backward"] = backward_timing(cfg, layer, x, ids, w, min(args.steps, 20), dev)
     if not args.skip_cpu_baseline:
         print("[bench] cpu baseline (oracle sample)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_sample_tokens)

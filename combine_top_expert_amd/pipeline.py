@@ -87,6 +87,19 @@ class MoELayer:
         self.y = torch.empty(s.T, s.H, dtype=_TORCH[s.out_dt], device=dev)
         self.w13 = self.w13_scales = self.w2 = self.w2_scales = self.w13_packed = None
 
+    def set_fused(self, fused: bool):
+        """Switch the gate/up GEMM between the fused SiLU*up epilogue (the
+        inference forward; a backward recomputes G) and the unfused pair
+        (stores fp32 G, which the backward then reuses)."""
+        s = self.shape
+        if not fused and self.g is None:
+            g = getattr(self, "g_saved", None)
+            self.g = g if g is not None else torch.empty(s.rows_cap, 2 * s.I, dtype=torch.float32,
+                                                         device=self.buf.device)
+        if fused:
+            self.g = None
+        self.fused = fused
+
     def set_weights(self, w13, w2, w13_scales=None, w2_scales=None, pack_w13=True):
         """Device weights in the pages' layouts.  With pack_w13 (the default)
         the gate/up weights are also packed once into the GEMM's staging
@@ -149,7 +162,9 @@ class MoELayer:
         if getattr(self, "d_out", None) is None:
             self.d_out = torch.empty(rc, s.H, dtype=gdt, device=dev)
             self.d_w = torch.empty(s.T, s.K, dtype=torch.float32, device=dev)
-            self.g_saved = torch.empty(rc, 2 * s.I, dtype=torch.float32, device=dev)
+            # G: the unfused forward keeps it; after the fused forward it is recomputed
+            self.g_saved = (self.g if self.g is not None
+                            else torch.empty(rc, 2 * s.I, dtype=torch.float32, device=dev))
             self.dz = torch.empty(rc, s.I, dtype=gdt, device=dev)
             self.dg = torch.empty(rc, 2 * s.I, dtype=gdt, device=dev)
             self.da = torch.empty(rc, s.H, dtype=gdt, device=dev)
@@ -159,9 +174,10 @@ class MoELayer:
 
     def backward_stages(self, dy, topk_weights, weight_grads=True):
         """The backward as (name, launch) pairs in run order, for dy [T,H]:
-        combine backward, dZ = d_out W2 (on W2^T), G recomputed, SiLU*up
-        backward, dA = dG W13 (on W13^T), permute backward, then with
-        weight_grads dW2 = d_out^T Z and dW13 = dG^T A per expert."""
+        combine backward, dZ = d_out W2 (on W2^T), G recomputed (only after
+        the fused forward: the unfused one keeps G), SiLU*up backward,
+        dA = dG W13 (on W13^T), permute backward, then with weight_grads
+        dW2 = d_out^T Z and dW13 = dG^T A per expert."""
         self.prepare_backward()
         w, lay = ((self.w13_packed, MOE_W_PACKED) if self.w13_packed is not None
                   else (self.w13, MOE_W_ROW_MAJOR))
@@ -180,6 +196,8 @@ class MoELayer:
                                                     self.offsets, self.da, workspace=self.gemm_workspace)),
             ("permute_bw", lambda: moe_permute_backward(self.da, self.slot_of, self.dx)),
         ]
+        if self.g is not None:
+            st = [x for x in st if x[0] != "gemm_g"]
         if weight_grads:
             st += [
                 ("wgrad_w2", lambda: moe_grouped_gemm_wgrad(self.d_out, self.z, self.counts,
@@ -194,7 +212,7 @@ class MoELayer:
         d_w [T,K]); with weight_grads also fills dw2 [L,H,I] = d_out^T Z and
         dw13 [L,2I,H] = dG^T A per expert.  Reuses the forward's routing
         (slot_of, counts, offsets), its permuted activations, Z and expert
-        outputs; G is recomputed."""
+        outputs; G is the unfused forward's, else recomputed."""
         for _, f in self.backward_stages(dy, topk_weights, weight_grads):
             f()
         return self.dx, self.d_w

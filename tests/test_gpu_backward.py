@@ -43,14 +43,17 @@ def _config(name):
     return get_config(name)
 
 
-CASES = ["toy_fp32", "share_fp32", "manyrow_fp32_small", "skewed_bf16_small", "manyrow_bf16_small"]
+# ":saved_g" runs the unfused forward, which keeps G for the backward (no recompute)
+CASES = ["toy_fp32", "share_fp32", "manyrow_fp32_small", "skewed_bf16_small", "manyrow_bf16_small",
+         "share_fp32:saved_g", "skewed_bf16_small:saved_g"]
 
 
-def _run(ep, name):
+def _run(ep, case):
     from combine_top_expert_amd.pipeline import MoELayer
+    name, _, mode = case.partition(":")
     cfg = _config(name)
     wl = make_workload(cfg)
-    layer = MoELayer(layer_shape(cfg))
+    layer = MoELayer(layer_shape(cfg), fused=(mode != "saved_g"))
     upload_weights(layer, wl)
     bf = cfg.act == "bf16"
     x = dev(wl.x, "bf16" if bf else None)
@@ -60,6 +63,8 @@ def _run(ep, name):
     dy32 = rng.standard_normal((cfg.T, cfg.H)).astype(np.float32)
     dy_vals = B.to_format(dy32, "bf16" if bf else "f32")
     dy = torch.from_numpy(dy_vals).cuda().to(torch.bfloat16 if bf else torch.float32)
+    names = [n for n, _ in layer.backward_stages(dy, w)]
+    assert ("gemm_g" in names) == (mode != "saved_g")
     dx, d_w = layer.backward(dy, w)
     torch.cuda.synchronize()
     return cfg, wl, layer, dy_vals, host_vals(dx), d_w.cpu().numpy()
