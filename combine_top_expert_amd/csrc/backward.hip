@@ -324,8 +324,10 @@ __device__ __forceinline__ int tr_offset(int col0, int lane) {
 typedef int v2i_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ v8bf_t tr_fragment(uint32_t addr) {
   v2i_t lo, hi;
+  // early-clobber outputs: the first read's destination must not share a
+  // register with the address the second read still needs
   asm volatile("ds_read_b64_tr_b16 %0, %2\n\tds_read_b64_tr_b16 %1, %2 offset:2048"
-               : "=v"(lo), "=v"(hi)
+               : "=&v"(lo), "=&v"(hi)
                : "v"(addr));
   const v2i_t both[2] = {lo, hi};
   return *reinterpret_cast<const v8bf_t*>(both);
