@@ -279,8 +279,10 @@ constexpr int kW2Tile = 256;
 // kW3Stages stages, each 32 rows x 256 columns of both operands in row-major
 // order (512 bytes per row, the layout in memory), keeps kW3Stages - 1 chunks
 // of loads in flight while one is multiplied.  Within a row the 16-byte chunk
-// c sits at position c ^ 2 * (row & 3), so that the four rows one transposed
-// read touches fall in four different 32-byte bank windows.  A matrix-core
+// c sits at position c ^ 2 * (row & 3) ^ 8 * ((row >> 3) & 1): the four rows
+// a 16-lane group's transposed read touches fall in four different 32-byte
+// bank windows, and the two groups served together (rows 8 apart) in
+// different 128-byte halves of the banks.  A matrix-core
 // operand (8 consecutive rows of one column) is two transposed LDS reads
 // (ds_read_b64_tr_b16: within 16 lanes, lane 4*d + q names row d, columns
 // 4q..4q+3, and lane j receives column j of those four rows).  Rows past the
@@ -311,10 +313,16 @@ typedef __attribute__((address_space(3))) void* lds_void_t;
 // byte offset, within one operand of a stage, of this lane's first transposed
 // read for the 16 columns starting at col0 (the second read is 4 rows = 2048
 // bytes further)
+__device__ __forceinline__ int chunk_swizzle(int row) {
+  // rows 4 apart share it (the second transposed read is 2048 bytes on)
+  return 2 * (row & 3) ^ 8 * ((row >> 3) & 1);
+}
+
 __device__ __forceinline__ int tr_offset(int col0, int lane) {
   const int g = lane >> 4, d = (lane >> 2) & 3, q = lane & 3;
   const int c = (col0 >> 3) + (q >> 1);                 // logical 16-byte chunk
-  return (8 * g + d) * 512 + ((c ^ (2 * d)) << 4) + ((q & 1) << 3);
+  const int row = 8 * g + d;
+  return row * 512 + ((c ^ chunk_swizzle(row)) << 4) + ((q & 1) << 3);
 }
 
 // Transposed reads are written as inline assembly: as compiler builtins they
@@ -358,7 +366,7 @@ __global__ __launch_bounds__(kW3Threads, 1) void wgrad_bf16_lds_kernel(
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int row = 4 * wave + 2 * j + (lane >> 5);
-    const int cl = (lane & 31) ^ (2 * (row & 3));
+    const int cl = (lane & 31) ^ chunk_swizzle(row);
     vB[j] = row * N * 2 + n0 * 2 + cl * 16;
     vA[j] = row * K * 2 + k0 * 2 + cl * 16;
   }
@@ -426,6 +434,9 @@ __global__ __launch_bounds__(kW3Threads, 1) void wgrad_bf16_lds_kernel(
     }
   }
   if (!active) return;
+  // lane holds C[n = 16x + 4 * (lane >> 4) + r][k = 16y + (lane & 15)]: each
+  // store writes 64 contiguous bytes of 4 rows (16-byte stores across 16 rows
+  // measured slower)
   float* ce = c + static_cast<int64_t>(e) * N * K;
 #pragma unroll
   for (int x = 0; x < 8; ++x)
@@ -448,7 +459,8 @@ extern "C" moe_status moe_grouped_gemm_wgrad(const void* b, const void* a, moe_d
   MOE_CHECK(dt != MOE_FP8_E4M3, MOE_ERR_UNSUPPORTED);
   MOE_CHECK(N % kWgTile == 0 && K % kWgTile == 0, MOE_ERR_UNSUPPORTED);
   MOE_CHECK(c && counts && offsets && (rows_cap == 0 || (a && b)), MOE_ERR_INVALID_ARG);
-  MOE_CHECK(((reinterpret_cast<uintptr_t>(a) | reinterpret_cast<uintptr_t>(b)) & 15) == 0, MOE_ERR_INVALID_ARG);
+  MOE_CHECK(((reinterpret_cast<uintptr_t>(a) | reinterpret_cast<uintptr_t>(b) | reinterpret_cast<uintptr_t>(c)) & 15) == 0,
+            MOE_ERR_INVALID_ARG);
   const dim3 grid(K / kWgTile, N / kWgTile, L);
   if (dt == MOE_F32)
     wgrad_f32_kernel<<<grid, kThreads, 0, stream>>>(static_cast<const float*>(b), static_cast<const float*>(a),

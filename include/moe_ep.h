@@ -358,7 +358,7 @@ moe_status moe_transpose_weights(const void* w, moe_dtype w_dt, int L, int N, in
  * [offsets[e], offsets[e] + counts[e]) (clamped to rows_cap); padding rows
  * are never read.  An expert without rows gets C[e] = 0.
  *   b [rows_cap,N], a [rows_cap,K] (dt, row-major, 16-byte aligned),
- *   c [L,N,K] fp32, caller-owned, every element written.
+ *   c [L,N,K] fp32 (16-byte aligned), caller-owned, every element written.
  * dtypes: F32 or BF16 (FP8 buffers: MOE_ERR_UNSUPPORTED).
  * Limits: N % 128 == 0, K % 128 == 0, L <= 65535.
  */

@@ -255,3 +255,4 @@ def test_backward_argument_errors(lib):
     assert wg(A, A, 1, A, A, 4, 64, 128, 128, None, None) == INVALID                    # no c
     assert wg(P(258), A, 1, A, A, 4, 64, 128, 128, A, None) == INVALID                  # misaligned b
     assert wg(A, None, 1, A, A, 4, 64, 128, 128, A, None) == INVALID                    # no a
+    assert wg(A, A, 1, A, A, 4, 64, 128, 128, P(260), None) == INVALID                  # misaligned c
