@@ -115,7 +115,14 @@ def cpu_baseline(wl, n_tokens):
         res = moe.moe_layer(wl, tokens=tokens, ew=moe.ExpertWeights(wl.cfg, wl.w, cache=False))
         dt = time.perf_counter() - t0
     rows = int((res["layout"]["slot_of"][tokens] >= 0).sum())
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), None)
+    except OSError:
+        pass
     return {"value": rows / dt, "unit": "rows/s", "cores": int(blas), "kind": "oracle",
+            "cpu_model": model, "host_cpus": os.cpu_count(),
             "sample": f"first {len(tokens)} of {wl.cfg.T} tokens ({rows} routed rows) of the same "
                       f"workload through the whole numpy oracle (layout, FP8 permute, per-expert "
                       f"weight dequantisation, fp64 GEMMs, combine); {dt:.1f} s"}
@@ -171,7 +178,9 @@ def _time_stages(stages, steps, dev):
     per = np.array([[ev[s][i].elapsed_time(ev[s][i + 1]) for i in range(len(stages))]
                     for s in range(steps)]) * 1e3
     return ({name: float(np.median(per[:, i])) for i, (name, _) in enumerate(stages)},
-            float(np.median(per.sum(axis=1))))
+            float(np.median(per.sum(axis=1))),
+            {name: [float(np.percentile(per[:, i], 10)), float(np.percentile(per[:, i], 90))]
+             for i, (name, _) in enumerate(stages)})
 
 
 def backward_timing(cfg, layer, x, ids, w, steps, dev):
@@ -188,14 +197,14 @@ def backward_timing(cfg, layer, x, ids, w, steps, dev):
     gb = {"bf16": 2, "f32": 4}[cfg.out_dt]
     dy = torch.randn(cfg.T, cfg.H, device=dev, generator=g).to(layer.out.dtype)
     layer.forward(x, ids, w)
-    us, total = _time_stages(layer.backward_stages(dy, w), steps, dev)
+    us, total, us_p = _time_stages(layer.backward_stages(dy, w), steps, dev)
     # unfused forward keeping G, then the backward without the recompute
     layer.set_fused(False)
     layer.forward(x, ids, w)
-    fwd_us, _ = _time_stages([("gemm_w13_store_g", layer.gemm_w13), ("silu_mul", layer.silu_mul)],
-                             steps, dev)
+    fwd_us, _, _ = _time_stages([("gemm_w13_store_g", layer.gemm_w13), ("silu_mul", layer.silu_mul)],
+                                steps, dev)
     layer.forward(x, ids, w)
-    us_saved, total_saved = _time_stages(layer.backward_stages(dy, w), steps, dev)
+    us_saved, total_saved, _ = _time_stages(layer.backward_stages(dy, w), steps, dev)
     layer.set_fused(True)
     layer.forward(x, ids, w)
 
@@ -213,7 +222,7 @@ def backward_timing(cfg, layer, x, ids, w, steps, dev):
         "permute_bw": rows * H * gb + T * H * gb + T * K * 4,
     }
     peak = MFMA_PEAK_TFLOPS[cfg.wdt]
-    res = {"us": us, "total_us": total, "rows": rows,
+    res = {"us": us, "p10_p90_us": us_p, "total_us": total, "rows": rows,
            "timing": "medians over the passes, an event between stages; after the fused forward "
                      "(G recomputed)",
            "tflops": {k: v / (us[k] * 1e-6) / 1e12 for k, v in flops.items()},
@@ -320,6 +329,8 @@ def main():
     counts = layer.counts.cpu().numpy()
     work = algorithmic_work(cfg, counts)
     stage_us = {k: float(np.median(per[:, i]) * 1e3) for i, k in enumerate(stages)}
+    stage_p10_p90 = {k: [float(np.percentile(per[:, i], 10) * 1e3), float(np.percentile(per[:, i], 90) * 1e3)]
+                     for i, k in enumerate(stages)}
     gemm_us = stage_us["gemm_w13"] + stage_us["gemm_w2"]
     peak_tf = MFMA_PEAK_TFLOPS[cfg.wdt]
     gemm_tflops = work["gemm_flops"] / (gemm_us * 1e-6) / 1e12
@@ -339,6 +350,7 @@ def main():
     roof["traffic"] = recorded_traffic(cfg.name)
     roof["kernel"] = "grouped_gemm_kernel (moe_grouped_gemm_w13, fused SiLU*up, FP8 Z)"
     roof["avg_us"] = w13_us
+    roof["p10_p90_us"] = [float(np.percentile(w13_launch_us, 10)), float(np.percentile(w13_launch_us, 90))]
     roof["algorithmic_bytes"] = work["w13_bytes"]
     roof["algorithmic_flops"] = work["w13_flops"]
     roof["mfma_frac"] = work["w13_flops"] / (w13_us * 1e-6) / 1e12 / peak_tf
@@ -365,6 +377,7 @@ def main():
         "gemm_tflops": gemm_tflops,
         "gemm_mfma_frac": gemm_tflops / peak_tf,
         "stage_us": stage_us,
+        "stage_p10_p90_us": stage_p10_p90,
         "stage_gbs": {
             "permute": None, "combine": None,
         },
