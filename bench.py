@@ -198,6 +198,7 @@ def backward_timing(cfg, layer, x, ids, w, steps, dev):
     dy = torch.randn(cfg.T, cfg.H, device=dev, generator=g).to(layer.out.dtype)
     layer.forward(x, ids, w)
     us, total, us_p = _time_stages(layer.backward_stages(dy, w), steps, dev)
+    tr_us, _, _ = _time_stages([("transpose_weights", layer.refresh_transposed_weights)], steps, dev)
     # unfused forward keeping G, then the backward without the recompute
     layer.set_fused(False)
     layer.forward(x, ids, w)
@@ -223,6 +224,8 @@ def backward_timing(cfg, layer, x, ids, w, steps, dev):
     }
     peak = MFMA_PEAK_TFLOPS[cfg.wdt]
     res = {"us": us, "p10_p90_us": us_p, "total_us": total, "rows": rows,
+           "transpose_weights_us": tr_us["transpose_weights"],
+           "transpose_note": "W2^T and W13^T, written once per weight update (not part of a pass)",
            "timing": "medians over the passes, an event between stages; after the fused forward "
                      "(G recomputed)",
            "tflops": {k: v / (us[k] * 1e-6) / 1e12 for k, v in flops.items()},

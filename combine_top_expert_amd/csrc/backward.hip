@@ -181,6 +181,40 @@ __global__ __launch_bounds__(kThreads) void transpose_kernel(const TE* __restric
   }
 }
 
+// bf16 transpose for N, K multiples of 64: thread t loads 16 bytes (8
+// elements) of rows t/8 and t/8 + 32 of the 64 x 64 tile, and writes 8
+// consecutive n of output rows k = t/8 and t/8 + 32 (8 lanes cover one output
+// row's 128 bytes), gathered from the LDS tile (row stride 66 elements).
+__global__ __launch_bounds__(kThreads) void transpose_bf16_vec_kernel(const uint16_t* __restrict__ w, int N,
+                                                                    int K, uint16_t* __restrict__ wt) {
+  constexpr int kStride = 66;
+  __shared__ uint16_t tile[64 * kStride];
+  const int e = blockIdx.z;
+  const int n0 = blockIdx.y * 64, k0 = blockIdx.x * 64;
+  const uint16_t* src = w + static_cast<int64_t>(e) * N * K;
+  uint16_t* dst = wt + static_cast<int64_t>(e) * N * K;
+  const int c = threadIdx.x & 7, r0 = threadIdx.x >> 3;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int r = r0 + 32 * h;
+    const uint4 v = *reinterpret_cast<const uint4*>(src + static_cast<int64_t>(n0 + r) * K + k0 + 8 * c);
+    const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i)       // 4-byte LDS writes: the row stride keeps them aligned
+      *reinterpret_cast<uint32_t*>(&tile[r * kStride + 8 * c + 2 * i]) = u[i];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int k = r0 + 32 * h;
+    uint32_t o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      o[i] = tile[(8 * c + 2 * i) * kStride + k] | (uint32_t(tile[(8 * c + 2 * i + 1) * kStride + k]) << 16);
+    *reinterpret_cast<uint4*>(dst + static_cast<int64_t>(k0 + k) * N + n0 + 8 * c) = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+}
+
 // ---------------------------------------------------------------- weight gradients
 // C[e] = B_e^T A_e over expert e's valid rows: B [rows_cap, N], A [rows_cap, K]
 // -> C [L, N, K] fp32.
@@ -550,6 +584,9 @@ extern "C" moe_status moe_transpose_weights(const void* w, moe_dtype w_dt, int L
   if (w_dt == MOE_F32)
     transpose_kernel<float><<<grid, kThreads, 0, stream>>>(static_cast<const float*>(w), N, K,
                                                            static_cast<float*>(wt));
+  else if (N % 64 == 0 && K % 64 == 0 && ((reinterpret_cast<uintptr_t>(w) | reinterpret_cast<uintptr_t>(wt)) & 15) == 0)
+    transpose_bf16_vec_kernel<<<grid, kThreads, 0, stream>>>(static_cast<const uint16_t*>(w), N, K,
+                                                             static_cast<uint16_t*>(wt));
   else
     transpose_kernel<uint16_t><<<grid, kThreads, 0, stream>>>(static_cast<const uint16_t*>(w), N, K,
                                                               static_cast<uint16_t*>(wt));

@@ -146,18 +146,19 @@ class MoELayer:
     # ---- backward (bf16 / fp32 layers)
     def prepare_backward(self):
         """Transposed weights and gradient buffers, made once (the weights are
-        transposed again whenever set_weights is called)."""
+        transposed again when set_weights installs new tensors; in-place
+        updates need refresh_transposed_weights)."""
         s = self.shape
         if s.wdt == "fp8":
             raise ValueError("the backward covers bf16 and fp32 layers")
         dev = self.buf.device
         gdt = self.out.dtype                       # gradients stored like the expert output
-        if getattr(self, "_wt_src", None) is not (self.w13, self.w2):
+        src = getattr(self, "_wt_src", None)
+        if src is None or src[0] is not self.w13 or src[1] is not self.w2:
             self.w2_t = torch.empty(s.L, s.I, s.H, dtype=self.w2.dtype, device=dev)
             self.w13_t = torch.empty(s.L, s.H, 2 * s.I, dtype=self.w13.dtype, device=dev)
-            moe_transpose_weights(self.w2, self.w2_t)
-            moe_transpose_weights(self.w13, self.w13_t)
             self._wt_src = (self.w13, self.w2)
+            self.refresh_transposed_weights()
         rc = s.rows_cap
         if getattr(self, "d_out", None) is None:
             self.d_out = torch.empty(rc, s.H, dtype=gdt, device=dev)
@@ -171,6 +172,14 @@ class MoELayer:
             self.dx = torch.empty(s.T, s.H, dtype=gdt, device=dev)
             self.dw2 = torch.empty(s.L, s.H, s.I, dtype=torch.float32, device=dev)
             self.dw13 = torch.empty(s.L, 2 * s.I, s.H, dtype=torch.float32, device=dev)
+
+    def refresh_transposed_weights(self):
+        """Rewrite W2^T and W13^T from the current weights.  prepare_backward
+        does it when set_weights installs new weight tensors; a caller that
+        updates the weights in place (an optimizer step) calls this before
+        the next backward."""
+        moe_transpose_weights(self.w2, self.w2_t)
+        moe_transpose_weights(self.w13, self.w13_t)
 
     def backward_stages(self, dy, topk_weights, weight_grads=True):
         """The backward as (name, launch) pairs in run order, for dy [T,H]:

@@ -137,10 +137,14 @@ def test_backward_end_to_end(ep, name):
     assert np.all(dx[no_local] == 0)
 
 
-def test_transpose_weights(ep):
+@pytest.mark.parametrize("shape", [(3, 200, 136), (3, 192, 320), (2, 2816, 4096)])
+def test_transpose_weights(ep, shape):
+    """Ragged sizes (element-wise kernel) and multiples of 64 (the 16-byte
+    bf16 kernel), including the skewed shape's W13."""
+    L, N, K = shape
     for dt in (torch.float32, torch.bfloat16):
-        w = torch.randn(3, 200, 136, device="cuda").to(dt)
-        wt = torch.empty(3, 136, 200, device="cuda", dtype=dt)
+        w = torch.randn(L, N, K, device="cuda").to(dt)
+        wt = torch.empty(L, K, N, device="cuda", dtype=dt)
         ep.moe_transpose_weights(w, wt)
         torch.cuda.synchronize()
         assert torch.equal(wt.cpu(), w.cpu().transpose(1, 2))
@@ -262,3 +266,48 @@ def test_backward_full_size_sampled(ep):
                 assert np.max(np.abs(got - ref)) <= 1e-4 * max(1.0, np.max(np.abs(ref))), (e, n)
     assert torch.isfinite(layer.dw13).all() and torch.isfinite(layer.dw2).all()
     print(f"[metric] backward full skewed_bf16: {len(tokens)} tokens, {len(rows)} rows checked", flush=True)
+
+
+@pytest.mark.parametrize("saved_g", [False, True])
+def test_backward_hip_graph_replay(ep, saved_g):
+    """Forward + backward captured once in a HIP graph; replayed with new
+    upstream gradients copied into the captured dy, eager work and syncs in
+    between.  Every replay must equal the eager result bit for bit (dx, d_w,
+    dW2, dW13)."""
+    from combine_top_expert_amd.pipeline import MoELayer
+    announce("backward hip graph", f"saved_g={saved_g}")
+    cfg = get_config("skewed_bf16_small")
+    wl = make_workload(cfg)
+    layer = MoELayer(layer_shape(cfg), fused=not saved_g)
+    upload_weights(layer, wl)
+    x, ids, w = dev(wl.x, "bf16"), dev(wl.ids), dev(wl.weights)
+    dy = torch.zeros(cfg.T, cfg.H, device="cuda", dtype=torch.bfloat16)
+
+    def step():
+        layer.forward(x, ids, w)
+        layer.backward(dy, w)
+
+    step()                                         # allocations and transposes outside capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            step()
+    torch.cuda.current_stream().wait_stream(s)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(3)
+    outs = lambda: [t.clone() for t in (layer.dx, layer.d_w, layer.dw2, layer.dw13)]
+    for rep in range(3):
+        dy.copy_(torch.randn(cfg.T, cfg.H, device="cuda", generator=gen).to(torch.bfloat16))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = outs()
+        step()
+        torch.cuda.synchronize()
+        ref = outs()
+        for a, b in zip(got, ref):
+            assert torch.equal(a, b), rep
+        assert torch.isfinite(ref[3]).all() and ref[3].abs().sum() > 0
