@@ -307,8 +307,6 @@ __global__ __launch_bounds__(kThreads) void wgrad_f32_kernel(const float* __rest
     }
 }
 
-constexpr int kW2Tile = 256;
-
 // bf16 weight gradients, staged by direct global-to-LDS loads.  A ring of
 // kW3Stages stages, each 32 rows x 256 columns of both operands in row-major
 // order (512 bytes per row, the layout in memory), keeps kW3Stages - 1 chunks
@@ -329,9 +327,10 @@ constexpr int kW2Tile = 256;
 // columns would read, and those waves skip both the products and the stores.
 // Blocks are numbered expert-major, then n tile, then k tile.
 constexpr int kW3Threads = 512;
+constexpr int kW3Tile = 256;                           // C tile: 256 x 256
 constexpr int kW3Rows = 32;
 constexpr int kW3Stages = 4;
-constexpr int kW3OpBytes = kW3Rows * kW2Tile * 2;       // one operand of one stage: 16 KB
+constexpr int kW3OpBytes = kW3Rows * kW3Tile * 2;       // one operand of one stage: 16 KB
 constexpr int kW3StageBytes = 2 * kW3OpBytes;
 constexpr int kW3LoadsPerChunk = 4;                     // per thread: 2 per operand
 constexpr uint32_t kW3RsrcWord3 = 0x00020000u;
@@ -340,8 +339,6 @@ template <int N> struct W3VmCnt {
   static constexpr int imm = (N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8);
 };
 
-typedef short v4s_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) v4s_t* lds_v4s_t;
 typedef __attribute__((address_space(3))) void* lds_void_t;
 
 // byte offset, within one operand of a stage, of this lane's first transposed
@@ -387,7 +384,7 @@ __global__ __launch_bounds__(kW3Threads, 1) void wgrad_bf16_lds_kernel(
   const int per_e = tiles_n * tiles_k;
   const int e = blockIdx.x / per_e;
   const int rem = blockIdx.x - e * per_e;
-  const int n0 = (rem / tiles_k) * kW2Tile, k0 = (rem % tiles_k) * kW2Tile;
+  const int n0 = (rem / tiles_k) * kW3Tile, k0 = (rem % tiles_k) * kW3Tile;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t off = offsets[e];
   int cnt = 0;
@@ -500,7 +497,7 @@ extern "C" moe_status moe_grouped_gemm_wgrad(const void* b, const void* a, moe_d
     wgrad_f32_kernel<<<grid, kThreads, 0, stream>>>(static_cast<const float*>(b), static_cast<const float*>(a),
                                                        counts, offsets, rows_cap, N, K, c);
   else {
-    const int tn = (N + kW2Tile - 1) / kW2Tile, tk = (K + kW2Tile - 1) / kW2Tile;
+    const int tn = (N + kW3Tile - 1) / kW3Tile, tk = (K + kW3Tile - 1) / kW3Tile;
     const int64_t blocks = static_cast<int64_t>(L) * tn * tk;
     MOE_CHECK(blocks <= INT32_MAX, MOE_ERR_UNSUPPORTED);
     MOE_CHECK(32LL * std::max(N, K) * 2 < (int64_t(1) << 31), MOE_ERR_UNSUPPORTED);   // per-chunk offsets
