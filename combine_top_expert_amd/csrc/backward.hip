@@ -104,6 +104,65 @@ __global__ __launch_bounds__(kThreads) void combine_backward_kernel(
   if (lane < K) d_w[static_cast<int64_t>(t) * K + lane] = dw_l;
 }
 
+// All-bf16 combine backward for H <= 4096: the lane's 8 chunks of dy[t] are
+// loaded once and stay in registers for every route of the token, and a
+// route's 8 chunks of out[q] (non-temporal: read once) are all issued before
+// any is used.  Per lane the products run in the same order as above, so d_out
+// and d_w are bit-identical to the general kernel.
+constexpr int kCbNper = 8;
+__global__ __launch_bounds__(kThreads) void combine_backward_bf16_reg_kernel(
+    const uint4* __restrict__ dy, const uint4* __restrict__ out, const int32_t* __restrict__ slot_of,
+    const float* __restrict__ w, int T, int K, int H, int64_t rows_cap, uint4* __restrict__ d_out,
+    float* __restrict__ d_w) {
+  const int lane = moe::lane_id();
+  const int t = blockIdx.x * kWavesPerBlock + threadIdx.x / MOE_WAVE;
+  if (t >= T) return;
+  const int s_l = lane < K ? slot_of[static_cast<int64_t>(t) * K + lane] : -1;
+  const float w_l = lane < K ? w[static_cast<int64_t>(t) * K + lane] : 0.f;
+  const uint64_t routes = __ballot(s_l >= 0 && s_l < rows_cap);
+  const int nchunk = H / 8;
+  const uint4* dyrow = dy + static_cast<int64_t>(t) * nchunk;
+  uint4 g[kCbNper];
+#pragma unroll
+  for (int j = 0; j < kCbNper; ++j) {
+    const int c = lane + MOE_WAVE * j;
+    g[j] = c < nchunk ? dyrow[c] : make_uint4(0, 0, 0, 0);
+  }
+  float dw_l = 0.f;
+  for (uint64_t m = routes; m; m &= m - 1) {
+    const int k = __builtin_ctzll(m);
+    const int q = __builtin_amdgcn_readlane(s_l, k);
+    const float wk = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w_l), k));
+    const uint4* orow = out + static_cast<int64_t>(q) * nchunk;
+    uint4* drow = d_out + static_cast<int64_t>(q) * nchunk;
+    uint4 o[kCbNper];
+#pragma unroll
+    for (int j = 0; j < kCbNper; ++j) {
+      const int c = lane + MOE_WAVE * j;
+      o[j] = c < nchunk ? moe::load_nt16(orow + c) : make_uint4(0, 0, 0, 0);
+    }
+    float dot = 0.f;
+#pragma unroll
+    for (int j = 0; j < kCbNper; ++j) {
+      const int c = lane + MOE_WAVE * j;
+      if (c >= nchunk) break;
+      float gf[8], of[8], d[8];
+      load8<false>(reinterpret_cast<const uint8_t*>(&g[j]), 0, gf);
+      load8<false>(reinterpret_cast<const uint8_t*>(&o[j]), 0, of);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        dot = fmaf(gf[i], of[i], dot);
+        d[i] = wk * gf[i];
+      }
+      store8<false>(reinterpret_cast<uint8_t*>(drow + c), 0, d);
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) dot += __shfl_xor(dot, off);
+    if (lane == k) dw_l = dot;
+  }
+  if (lane < K) d_w[static_cast<int64_t>(t) * K + lane] = dw_l;
+}
+
 // d_gate = dz * up * s * (1 + gate * (1 - s)), d_up = dz * SiLU(gate),
 // s = sigmoid(gate) from the hardware exp2 and reciprocal; one wave per valid
 // row, 4 columns per lane per step.
@@ -529,6 +588,13 @@ extern "C" moe_status moe_combine_backward(const void* dy, moe_dtype dy_dt, cons
 #define MOE_CB(A, B, C)                                                                                 \
   combine_backward_kernel<A, B, C><<<grid, kThreads, 0, stream>>>(g, o, slot_of, topk_weights, T, K, H, \
                                                                   rows_cap, d, d_weights)
+  if (sel == 0 && H <= 8 * MOE_WAVE * kCbNper) {
+    combine_backward_bf16_reg_kernel<<<grid, kThreads, 0, stream>>>(
+        static_cast<const uint4*>(dy), static_cast<const uint4*>(expert_out), slot_of, topk_weights, T, K, H,
+        rows_cap, static_cast<uint4*>(d_out), d_weights);
+    MOE_LAUNCH_CHECK();
+    return MOE_OK;
+  }
   switch (sel) {
     case 0: MOE_CB(false, false, false); break;
     case 1: MOE_CB(false, false, true); break;
