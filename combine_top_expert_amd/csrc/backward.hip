@@ -166,6 +166,7 @@ __global__ __launch_bounds__(kThreads) void combine_backward_bf16_reg_kernel(
 // d_gate = dz * up * s * (1 + gate * (1 - s)), d_up = dz * SiLU(gate),
 // s = sigmoid(gate) from the hardware exp2 and reciprocal; one wave per valid
 // row, 4 columns per lane per step.
+constexpr int kSiluBwBatch = 6;
 template <bool kDzF32, bool kDgF32>
 __global__ __launch_bounds__(kThreads) void silu_mul_backward_kernel(
     const float* __restrict__ g, const uint8_t* __restrict__ dz, const int32_t* __restrict__ counts,
@@ -184,36 +185,50 @@ __global__ __launch_bounds__(kThreads) void silu_mul_backward_kernel(
   const float* grow = g + q * 2 * I;
   const uint8_t* zrow = dz + q * I * (kDzF32 ? 4 : 2);
   uint8_t* drow = dg + q * 2 * I * (kDgF32 ? 4 : 2);
-  for (int c = lane; c < I / 4; c += MOE_WAVE) {
-    const float4 gt = reinterpret_cast<const float4*>(grow)[c];
-    const float4 up = reinterpret_cast<const float4*>(grow + I)[c];
-    float z[4];
-    if constexpr (kDzF32) {
-      const float4 v = reinterpret_cast<const float4*>(zrow)[c];
-      z[0] = v.x; z[1] = v.y; z[2] = v.z; z[3] = v.w;
-    } else {
-      const uint2 v = reinterpret_cast<const uint2*>(zrow)[c];
-      z[0] = __uint_as_float(v.x << 16); z[1] = __uint_as_float(v.x & 0xffff0000u);
-      z[2] = __uint_as_float(v.y << 16); z[3] = __uint_as_float(v.y & 0xffff0000u);
-    }
-    const float ga[4] = {gt.x, gt.y, gt.z, gt.w}, ua[4] = {up.x, up.y, up.z, up.w};
-    float dgate[4], dup[4];
+  // a lane's steps in batches of kSiluBwBatch: every load of a batch is issued
+  // before any of its values is used
+  const int nstep = I / 4;
+  for (int base = lane; base < nstep; base += MOE_WAVE * kSiluBwBatch) {
+    float4 gt[kSiluBwBatch], up[kSiluBwBatch];
+    float z[kSiluBwBatch][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float s = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(ga[i] * -1.44269504088896341f));
-      dup[i] = z[i] * (ga[i] * s);
-      dgate[i] = z[i] * ua[i] * s * (1.0f + ga[i] * (1.0f - s));
+    for (int b = 0; b < kSiluBwBatch; ++b) {
+      const int c = base + MOE_WAVE * b;
+      const bool live = c < nstep;
+      gt[b] = live ? reinterpret_cast<const float4*>(grow)[c] : make_float4(0.f, 0.f, 0.f, 0.f);
+      up[b] = live ? reinterpret_cast<const float4*>(grow + I)[c] : make_float4(0.f, 0.f, 0.f, 0.f);
+      if constexpr (kDzF32) {
+        const float4 v = live ? reinterpret_cast<const float4*>(zrow)[c] : make_float4(0.f, 0.f, 0.f, 0.f);
+        z[b][0] = v.x; z[b][1] = v.y; z[b][2] = v.z; z[b][3] = v.w;
+      } else {
+        const uint2 v = live ? reinterpret_cast<const uint2*>(zrow)[c] : make_uint2(0, 0);
+        z[b][0] = __uint_as_float(v.x << 16); z[b][1] = __uint_as_float(v.x & 0xffff0000u);
+        z[b][2] = __uint_as_float(v.y << 16); z[b][3] = __uint_as_float(v.y & 0xffff0000u);
+      }
     }
-    if constexpr (kDgF32) {
-      reinterpret_cast<float4*>(drow)[c] = make_float4(dgate[0], dgate[1], dgate[2], dgate[3]);
-      reinterpret_cast<float4*>(drow + I * 4)[c] = make_float4(dup[0], dup[1], dup[2], dup[3]);
-    } else {
-      reinterpret_cast<uint2*>(drow)[c] = make_uint2(
-          moe::f32_to_bf16(dgate[0]) | (uint32_t(moe::f32_to_bf16(dgate[1])) << 16),
-          moe::f32_to_bf16(dgate[2]) | (uint32_t(moe::f32_to_bf16(dgate[3])) << 16));
-      reinterpret_cast<uint2*>(drow + I * 2)[c] = make_uint2(
-          moe::f32_to_bf16(dup[0]) | (uint32_t(moe::f32_to_bf16(dup[1])) << 16),
-          moe::f32_to_bf16(dup[2]) | (uint32_t(moe::f32_to_bf16(dup[3])) << 16));
+#pragma unroll
+    for (int b = 0; b < kSiluBwBatch; ++b) {
+      const int c = base + MOE_WAVE * b;
+      if (c >= nstep) break;
+      const float ga[4] = {gt[b].x, gt[b].y, gt[b].z, gt[b].w}, ua[4] = {up[b].x, up[b].y, up[b].z, up[b].w};
+      float dgate[4], dup[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float s = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(ga[i] * -1.44269504088896341f));
+        dup[i] = z[b][i] * (ga[i] * s);
+        dgate[i] = z[b][i] * ua[i] * s * (1.0f + ga[i] * (1.0f - s));
+      }
+      if constexpr (kDgF32) {
+        reinterpret_cast<float4*>(drow)[c] = make_float4(dgate[0], dgate[1], dgate[2], dgate[3]);
+        reinterpret_cast<float4*>(drow + I * 4)[c] = make_float4(dup[0], dup[1], dup[2], dup[3]);
+      } else {
+        reinterpret_cast<uint2*>(drow)[c] = make_uint2(
+            moe::f32_to_bf16(dgate[0]) | (uint32_t(moe::f32_to_bf16(dgate[1])) << 16),
+            moe::f32_to_bf16(dgate[2]) | (uint32_t(moe::f32_to_bf16(dgate[3])) << 16));
+        reinterpret_cast<uint2*>(drow + I * 2)[c] = make_uint2(
+            moe::f32_to_bf16(dup[0]) | (uint32_t(moe::f32_to_bf16(dup[1])) << 16),
+            moe::f32_to_bf16(dup[2]) | (uint32_t(moe::f32_to_bf16(dup[3])) << 16));
+      }
     }
   }
 }
