@@ -34,6 +34,7 @@ __device__ __forceinline__ bool valid_row(const int32_t* counts, const int32_t* 
   return q < static_cast<int64_t>(offsets[lo]) + counts[lo];
 }
 
+constexpr int kSiluBatch = 6;
 template <int ZDT>  // 0 f32, 1 bf16, 2 fp8
 __global__ __launch_bounds__(kThreads) void silu_mul_kernel(const float* __restrict__ g,
                                                             const int32_t* __restrict__ counts,
@@ -46,35 +47,47 @@ __global__ __launch_bounds__(kThreads) void silu_mul_kernel(const float* __restr
   if (q >= rows_cap || !valid_row(counts, offsets, L, q)) return;
   const float4* grow = reinterpret_cast<const float4*>(g + q * 2 * I);
   const int nchunk = I / 4;                       // 4 columns per lane-step
-  for (int c0 = 0; c0 < nchunk; c0 += MOE_WAVE) {
-    const int c = c0 + lane;
-    const bool live = c < nchunk;                 // nchunk % 32 == 0: groups stay whole
-    float4 gt = make_float4(0.f, 0.f, 0.f, 0.f), up = gt;
-    if (live) {
-      gt = grow[c];
-      up = grow[nchunk + c];
+  // steps in batches of kSiluBatch: a batch's loads are issued before any is used
+  for (int cb = 0; cb < nchunk; cb += MOE_WAVE * kSiluBatch) {
+    float4 gtb[kSiluBatch], upb[kSiluBatch];
+#pragma unroll
+    for (int b = 0; b < kSiluBatch; ++b) {
+      const int c = cb + MOE_WAVE * b + lane;
+      gtb[b] = upb[b] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (c < nchunk) {
+        gtb[b] = grow[c];
+        upb[b] = grow[nchunk + c];
+      }
     }
-    const float v[4] = {moe::silu(gt.x) * up.x, moe::silu(gt.y) * up.y, moe::silu(gt.z) * up.z,
-                        moe::silu(gt.w) * up.w};
-    if constexpr (ZDT == 2) {
-      float m = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
-      m = moe::group16_max(m);
-      m = fmaxf(m, __shfl_xor(m, 16));
-      const float amax = moe::fp8_group_amax_clamp(m);
-      const float inv = moe::fp8_group_inv(amax);
-      if (live) {
-        reinterpret_cast<uint32_t*>(z + q * I)[c] =
-            moe::f32x4_to_e4m3(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
-        if ((lane & 31) == 0) zs[q * (I / 128) + c / 32] = moe::fp8_group_scale(amax);
+#pragma unroll
+    for (int b = 0; b < kSiluBatch; ++b) {
+      const int c0 = cb + MOE_WAVE * b;
+      if (c0 >= nchunk) break;                      // wave-uniform
+      const int c = c0 + lane;
+      const bool live = c < nchunk;                 // nchunk % 32 == 0: groups stay whole
+      const float4 gt = gtb[b], up = upb[b];
+      const float v[4] = {moe::silu(gt.x) * up.x, moe::silu(gt.y) * up.y, moe::silu(gt.z) * up.z,
+                          moe::silu(gt.w) * up.w};
+      if constexpr (ZDT == 2) {
+        float m = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+        m = moe::group16_max(m);
+        m = fmaxf(m, __shfl_xor(m, 16));
+        const float amax = moe::fp8_group_amax_clamp(m);
+        const float inv = moe::fp8_group_inv(amax);
+        if (live) {
+          reinterpret_cast<uint32_t*>(z + q * I)[c] =
+              moe::f32x4_to_e4m3(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
+          if ((lane & 31) == 0) zs[q * (I / 128) + c / 32] = moe::fp8_group_scale(amax);
+        }
+      } else if constexpr (ZDT == 1) {
+        if (live) {
+          const uint32_t lo = moe::f32_to_bf16(v[0]) | (uint32_t(moe::f32_to_bf16(v[1])) << 16);
+          const uint32_t hi = moe::f32_to_bf16(v[2]) | (uint32_t(moe::f32_to_bf16(v[3])) << 16);
+          reinterpret_cast<uint2*>(z + q * I * 2)[c] = make_uint2(lo, hi);
+        }
+      } else {
+        if (live) reinterpret_cast<float4*>(z + q * I * 4)[c] = make_float4(v[0], v[1], v[2], v[3]);
       }
-    } else if constexpr (ZDT == 1) {
-      if (live) {
-        const uint32_t lo = moe::f32_to_bf16(v[0]) | (uint32_t(moe::f32_to_bf16(v[1])) << 16);
-        const uint32_t hi = moe::f32_to_bf16(v[2]) | (uint32_t(moe::f32_to_bf16(v[3])) << 16);
-        reinterpret_cast<uint2*>(z + q * I * 2)[c] = make_uint2(lo, hi);
-      }
-    } else {
-      if (live) reinterpret_cast<float4*>(z + q * I * 4)[c] = make_float4(v[0], v[1], v[2], v[3]);
     }
   }
 }
