@@ -150,16 +150,17 @@ def test_transpose_weights(ep, shape):
         assert torch.equal(wt.cpu(), w.cpu().transpose(1, 2))
 
 
+@pytest.mark.parametrize("N,K", [(256, 384), (384, 256)])
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
-def test_wgrad_ragged_experts(ep, dt):
+def test_wgrad_ragged_experts(ep, dt, N, K):
     """Ragged expert row counts (0, 1, one chunk short, one chunk over, many
-    chunks), padding rows filled with NaN (never read), several tiles in both
-    output dimensions: against float64 per expert."""
-    announce("wgrad ragged", dt)
+    chunks), padding rows filled with NaN (never read), several tiles and a
+    128-column tail in either output dimension: against float64 per expert."""
+    announce("wgrad ragged", dt, f"N={N} K={K}")
     counts = np.array([0, 1, 31, 33, 100, 0, 257], np.int32)
     R = 288                                   # capacity per expert; rows past the count are padding
     offsets = (np.arange(len(counts)) * R).astype(np.int32)
-    rows_cap, N, K = R * len(counts), 256, 384
+    rows_cap = R * len(counts)
     rng = np.random.default_rng(21)
     b = np.full((rows_cap, N), np.nan, np.float32)
     a = np.full((rows_cap, K), np.nan, np.float32)
@@ -311,3 +312,36 @@ def test_backward_hip_graph_replay(ep, saved_g):
         for a, b in zip(got, ref):
             assert torch.equal(a, b), rep
         assert torch.isfinite(ref[3]).all() and ref[3].abs().sum() > 0
+
+
+@pytest.mark.parametrize("H", [512, 4608])
+def test_combine_backward_direct(ep, H):
+    """moe_combine_backward on its own, all bf16: H = 512 takes the
+    register-cached kernel, H = 4608 the general one.  Non-local routes
+    (slot -1) and padding rows; d_out bit-exact, d_w within 1e-5."""
+    announce("combine backward", f"H={H}")
+    rng = np.random.default_rng(H)
+    T, K, rows_cap = 96, 6, 640
+    slot_of = np.full((T, K), -1, np.int32)
+    perm = rng.permutation(rows_cap)[: T * K].reshape(T, K)
+    keep = rng.random((T, K)) < 0.7
+    slot_of[keep] = perm[keep]
+    weights = rng.random((T, K)).astype(np.float32)
+    dy = B.to_format(rng.standard_normal((T, H)).astype(np.float32), "bf16")
+    out = B.to_format(rng.standard_normal((rows_cap, H)).astype(np.float32), "bf16")
+    rows = sorted(int(q) for q in slot_of[slot_of >= 0])
+    d_out_ref, d_w_ref = B.combine_backward(dy, {q: out[q] for q in rows}, slot_of, weights, "bf16")
+    bf = torch.bfloat16
+    d_out = torch.full((rows_cap, H), float("nan"), device="cuda", dtype=bf)
+    d_w = torch.full((T, K), 7.0, device="cuda")
+    ep.moe_combine_backward(torch.from_numpy(dy).cuda().to(bf), torch.from_numpy(out).cuda().to(bf),
+                            dev(slot_of), dev(weights), d_out, d_w)
+    torch.cuda.synchronize()
+    got = host_vals(d_out)
+    assert np.array_equal(np.stack([got[q] for q in rows]).view(np.uint32),
+                          np.stack([d_out_ref[q] for q in rows]).view(np.uint32))
+    untouched = np.setdiff1d(np.arange(rows_cap), rows)
+    assert np.isnan(got[untouched]).all()
+    dw = d_w.cpu().numpy()
+    assert np.all(dw[slot_of < 0] == 0)
+    assert rel_l2(dw, d_w_ref) < 1e-5
