@@ -243,7 +243,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU's share of the MoE layer; --gpus {args.gpus} is not "
-              "supported (multi-GPU expert-parallel exchange is not part of this build)",
+              "supported (the multi-GPU expert-parallel exchange is not implemented)",
               file=sys.stderr)
         sys.exit(2)
 
