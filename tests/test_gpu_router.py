@@ -61,6 +61,22 @@ def test_router_small_all_tokens(ep, E, K, mode):
     check(ids, w, x, K, bias, biw)
 
 
+@pytest.mark.parametrize("E,K,T", [(256, 8, 16384), (200, 16, 16400), (128, 16, 1000), (64, 6, 1001)])
+@pytest.mark.parametrize("mode", ["bias", "ties"])
+def test_router_segmented_kernel(ep, E, K, T, mode):
+    """Shapes that take the 16-lane-segment kernel (E <= 128, or E <= 256 with
+    at least 16384 tokens), with a token count that leaves the last wave's
+    segments partly empty: ids exact, weights to the bar."""
+    announce("router seg", E, K, T, mode)
+    rng = np.random.default_rng(E * 7 + K + T)
+    x = rng.standard_normal((T, E)).astype(np.float32)
+    if mode == "ties":
+        x = (np.round(x * 2) / 2).astype(np.float32)
+    bias = (0.5 * rng.standard_normal(E)).astype(np.float32) if mode == "bias" else None
+    ids, w = run(ep, x, K, bias, True)
+    check(ids, w, x, K, bias, True)
+
+
 def test_router_special_values(ep):
     announce("router special values")
     x = np.array([[np.nan, -np.inf, 0.0, -0.0, 1.0, 1.0, -1.0, np.inf]], np.float32)
