@@ -77,17 +77,13 @@ __global__ __launch_bounds__(kThreads) void router_topk_kernel(const float* __re
   float my_v = 0.0f;
   for (int k = 0; k < K; ++k) {
     uint64_t best = 0;
-    int bj = -1;
 #pragma unroll
-    for (int j = 0; j < NPL; ++j)
-      if (key[j] > best) { best = key[j]; bj = j; }
+    for (int j = 0; j < NPL; ++j) best = key[j] > best ? key[j] : best;
     const uint64_t win = wave_max_u64(best);
     const int e = static_cast<int>(0xffffffffu - static_cast<uint32_t>(win));
-    if (bj >= 0 && best == win) {               // the owning lane retires the winner
+    // keys are unique (the expert id is part of them): the owner retires it
 #pragma unroll
-      for (int j = 0; j < NPL; ++j)
-        if (j == bj) key[j] = 0;
-    }
+    for (int j = 0; j < NPL; ++j) key[j] = key[j] == win ? 0 : key[j];
     if (lane == k) my_id = e;
   }
   // the value entering the weights: the score, or the unbiased logit when
