@@ -166,11 +166,24 @@ def weight_values(w: np.ndarray, wdt: str, scales: np.ndarray | None = None) -> 
 
 # ============================================================== stages 3-5: expert MLP
 
-def gemm_w13(a_vals: np.ndarray, w13_vals: np.ndarray) -> np.ndarray:
+def _dot_rows(a_vals: np.ndarray, w_vals: np.ndarray, acc: str) -> np.ndarray:
+    """Every dot product of a row of A with a row of W, rounded to fp32.
+    acc="f64": float64 dot products rounded once (the oracle's definition);
+    acc="f32": the same operands summed in fp32 by the BLAS routine, an
+    evaluation order a correct fp32 implementation may also take.  The second
+    form only measures how much the format's roundings downstream react to
+    fp32-level differences; no result is checked against it."""
+    if acc == "f64":
+        return (np.asarray(a_vals, np.float64) @ np.asarray(w_vals, np.float64).T).astype(np.float32)
+    assert acc == "f32", acc
+    return np.asarray(a_vals, np.float32) @ np.asarray(w_vals, np.float32).T
+
+
+def gemm_w13(a_vals: np.ndarray, w13_vals: np.ndarray, acc: str = "f64") -> np.ndarray:
     """G = A W13^T for one expert's valid rows ([ECB] §1.1: X_e [m_e, H] ->
     gate/up GEMM -> [m_e, 2I]; weights stored [expert, out, in], §3.5).
     float64 dot products, rounded once to fp32."""
-    return (a_vals @ w13_vals.T).astype(np.float32)
+    return _dot_rows(a_vals, w13_vals, acc)
 
 
 def silu(v: np.ndarray) -> np.ndarray:
@@ -199,10 +212,10 @@ def z_to_format(z: np.ndarray, z_dt: str) -> dict:
     return {"data": np.asarray(z, np.float32)}
 
 
-def gemm_w2(z_vals: np.ndarray, w2_vals: np.ndarray) -> np.ndarray:
+def gemm_w2(z_vals: np.ndarray, w2_vals: np.ndarray, acc: str = "f64") -> np.ndarray:
     """out = Z W2^T ([ECB] §1.1: [m_e, I] -> down GEMM -> [m_e, H]), float64
     dot products rounded once to fp32."""
-    return (z_vals @ w2_vals.T).astype(np.float32)
+    return _dot_rows(z_vals, w2_vals, acc)
 
 
 def out_to_format(out: np.ndarray, out_dt: str) -> np.ndarray:
@@ -263,10 +276,12 @@ class ExpertWeights:
         return self._get(self._c2, "w2", e)
 
 
-def expert_mlp_rows(cfg, a_vals_by_row: dict, expert_of_row: dict, ew: ExpertWeights) -> dict:
+def expert_mlp_rows(cfg, a_vals_by_row: dict, expert_of_row: dict, ew: ExpertWeights,
+                    acc: str = "f64") -> dict:
     """Run GEMM-1 -> SiLU*up -> Z rounding -> GEMM-2 on the given rows, each
     with its own expert's weights.  Returns per-row dicts of G (fp32), Z in
-    its format, and the expert output (fp32 values of the output format)."""
+    its format, and the expert output (fp32 values of the output format).
+    ``acc`` selects the dot products' accumulation (see _dot_rows)."""
     res = {"G": {}, "Z": {}, "Zs": {}, "out": {}}
     by_e: dict[int, list] = {}
     for q, e in expert_of_row.items():
@@ -274,11 +289,11 @@ def expert_mlp_rows(cfg, a_vals_by_row: dict, expert_of_row: dict, ew: ExpertWei
     for e, qs in sorted(by_e.items()):
         qs = sorted(qs)
         a = np.stack([a_vals_by_row[q] for q in qs])
-        g = gemm_w13(a, ew.w13(e))
+        g = gemm_w13(a, ew.w13(e), acc)
         z = silu_mul(g, cfg.I)
         zf = z_to_format(z, cfg.z_dt)
         zv = buffer_values(zf["data"], cfg.z_dt, zf.get("scales"))
-        out = out_to_format(gemm_w2(zv, ew.w2(e)), cfg.out_dt)
+        out = out_to_format(gemm_w2(zv, ew.w2(e), acc), cfg.out_dt)
         for i, q in enumerate(qs):
             res["G"][q] = g[i]
             res["Z"][q] = zf["data"][i]
@@ -288,12 +303,14 @@ def expert_mlp_rows(cfg, a_vals_by_row: dict, expert_of_row: dict, ew: ExpertWei
     return res
 
 
-def moe_layer(wl, tokens=None, BM: int = 128, ew: ExpertWeights | None = None) -> dict:
+def moe_layer(wl, tokens=None, BM: int = 128, ew: ExpertWeights | None = None,
+              acc: str = "f64") -> dict:
     """dispatch_layout -> permute -> expert MLP -> combine for a workload.
 
     ``tokens`` restricts the expert MLP and combine to the routes of those
     tokens (layout is always computed in full, it is cheap); the outputs for
-    those tokens are then exactly what the full computation gives them."""
+    those tokens are then exactly what the full computation gives them.
+    ``acc`` selects the dot products' accumulation (see _dot_rows)."""
     cfg = wl.cfg
     ew = ew or ExpertWeights(cfg, wl.w)
     if cfg.routing == "given":
@@ -319,7 +336,7 @@ def moe_layer(wl, tokens=None, BM: int = 128, ew: ExpertWeights | None = None) -
         assert offsets[e] <= q < offsets[e] + counts[e]
         e_of[int(q)] = e
     a_by_row = {int(q): a_vals[i] for i, q in enumerate(perm["rows"])}
-    mlp = expert_mlp_rows(cfg, a_by_row, e_of, ew)
+    mlp = expert_mlp_rows(cfg, a_by_row, e_of, ew, acc)
     y = combine(mlp["out"], slot_of, wl.weights, cfg.out_dt, tokens=sel)
     return {"layout": lay, "perm": perm, "mlp": mlp, "y": y, "tokens": sel}
 
