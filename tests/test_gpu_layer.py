@@ -1,17 +1,19 @@
 """GPU parity of the whole layer (all six entry points) against the oracle.
 
-Bar: relative L2 error <= 2e-2 and max-abs error / max|ref| <= 5e-2 on the
-layer output y (both printed, with max-abs / RMS(ref), per case); layout
-bit-exact.  Small shapes compare every token; the
-full shapes (decode, prefill, skewed) run in the launch configuration the
-benchmark times and compare tokens sampled so that the oracle can compute
-each one directly."""
+Every case runs gpu_util.check_layer: layout bit-exact; every Z element of
+the compared rows a correct rounding of the oracle's z within the G error
+bound (FP8 codes and scales included); every expert-output element within
+the down GEMM's bound of the oracle's result on the GPU's Z; combine
+bit-exact on the GPU's expert outputs; and the layer bars (rel-L2 <= 2e-2
+against the oracle; max|dy|/RMS <= 5e-2 against the oracle on the GPU's Z,
+and <= max(5e-2, 3 x the oracle's own fp32-vs-float64 figure) against the
+oracle's y).  Small shapes compare every token; the full shapes are in
+tests/test_gpu_full_size.py."""
 import numpy as np
 import pytest
 import torch
 
-from gpu_util import (LAYER_MAXABS, LAYER_REL_L2, announce, dev, host_vals, layer_shape,
-                      maxabs_over_rms, maxabs_rel, need_gpu, rel_l2, upload_weights)
+from gpu_util import announce, check_layer, dev, host_vals, layer_shape, need_gpu, upload_weights
 from oracle import moe
 from workloads import get_config, make_workload
 
@@ -57,14 +59,6 @@ def run_share(ep, layer, wl):
     return host_vals(layer.y)
 
 
-def check(y, ref, tag=""):
-    print(f"[metric] {tag} rel_l2={rel_l2(y, ref):.3e} maxabs/max={maxabs_rel(y, ref):.3e} "
-          f"maxabs/rms={maxabs_over_rms(y, ref):.3e}", flush=True)
-    assert np.all(np.isfinite(y))
-    assert rel_l2(y, ref) <= LAYER_REL_L2, rel_l2(y, ref)
-    assert maxabs_rel(y, ref) <= LAYER_MAXABS, maxabs_rel(y, ref)
-
-
 @pytest.mark.parametrize("fused", [True, False])
 @pytest.mark.parametrize("name", ["toy_fp32", "share_bf16", "toy_bf16_fp8w", "decode_fp8_small",
                                   "prefill_fp8_small", "skewed_bf16_small", "manyrow_bf16_small",
@@ -73,28 +67,11 @@ def test_layer_small_all_tokens(ep, name, fused):
     announce("layer", name, "fused" if fused else "unfused")
     wl = make_workload(name)
     layer = build(wl, fused)
-    y = run_share(ep, layer, wl) if wl.cfg.routing == "given" else run(layer, wl)
-    ref = moe.moe_layer(wl)["y"]
-    check(y, ref, f"{name} fused={fused}")
-    if wl.cfg.routing != "given":
-        lay = moe.dispatch_layout(wl.ids, wl.cfg.E, wl.cfg.expert_begin, wl.cfg.L, wl.cfg.R)
-        assert np.array_equal(layer.slot_of.cpu().numpy(), lay["slot_of"])
-
-
-@pytest.mark.parametrize("name,n_tok", [("decode_fp8", 128), ("prefill_fp8", 12), ("skewed_bf16", 12)])
-def test_layer_full_size_sampled(ep, name, n_tok):
-    announce("layer full", name)
-    wl = make_workload(name)
-    layer = build(wl, fused=True)
-    y = run(layer, wl)
-    T = wl.cfg.T
-    rng = np.random.default_rng(2024)
-    tokens = np.arange(T) if n_tok >= T else np.sort(rng.choice(T, n_tok, replace=False))
-    if name == "skewed_bf16":      # make sure the hottest expert's tail tile is covered
-        hot = np.nonzero((wl.ids == 0).any(axis=1))[0]
-        tokens = np.unique(np.concatenate([tokens, hot[-2:]]))
-    ref = moe.moe_layer(wl, tokens=tokens, ew=moe.ExpertWeights(wl.cfg, wl.w, cache=False))["y"]
-    check(y[tokens], ref, name)
+    if wl.cfg.routing == "given":
+        run_share(ep, layer, wl)
+    else:
+        run(layer, wl)
+    check_layer(wl, layer, tag=f"{name} fused={fused}")
 
 
 def test_layer_replay_new_routing(ep):
@@ -103,12 +80,12 @@ def test_layer_replay_new_routing(ep):
     announce("layer replay")
     wl = make_workload("toy_fp32")
     layer = build(wl)
-    y1 = run(layer, wl)
-    check(y1, moe.moe_layer(wl)["y"])
+    run(layer, wl)
+    check_layer(wl, layer, tag="toy replay 1")
     wl.ids = wl.ids.copy()
     wl.ids[5] = [0, 7]
-    y2 = run(layer, wl)
-    check(y2, moe.moe_layer(wl)["y"])
+    run(layer, wl)
+    check_layer(wl, layer, tag="toy replay 2")
     c = layer.counts.cpu().numpy()
     assert [c[0], c[1], c[6], c[7]] == [112, 0, 0, 112]
 
@@ -174,4 +151,4 @@ def test_hip_graph_replay(ep):
         assert np.array_equal(y_graph, y_eager), rep
         wl2 = make_workload(cfg)
         wl2.ids = new_ids
-        check(y_eager, moe.moe_layer(wl2)["y"])
+        check_layer(wl2, layer, tag=f"graph replay {rep}")
