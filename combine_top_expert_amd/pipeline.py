@@ -226,6 +226,40 @@ class MoELayer:
             f()
         return self.dx, self.d_w
 
+    def bind_forward(self, x, topk_ids, topk_weights):
+        """The forward's launches as (name, callable) pairs, each marshalled
+        once (shapes checked, pointers and the current stream looked up), so
+        calling them runs the path with a few microseconds of host time per
+        launch.  The tensors must stay alive and unchanged in shape."""
+        s = self.shape
+        w, lay = ((self.w13_packed, MOE_W_PACKED) if self.w13_packed is not None
+                  else (self.w13, MOE_W_ROW_MAJOR))
+        st = [
+            ("layout", moe_dispatch_layout(topk_ids, s.E, s.expert_begin, s.L, s.R, s.BM, self.counts,
+                                           self.offsets, self.slot_of, self.row_src, self.tile_offsets,
+                                           self.dev_status, self.workspace, bind=True)),
+            ("permute", moe_permute(x, self.slot_of, self.buf, self.buf_scales, bind=True)),
+        ]
+        if self.fused:
+            st.append(("gemm_w13", moe_grouped_gemm_w13(self.buf, self.buf_scales, w, self.w13_scales,
+                                                         self.counts, self.offsets, MOE_EPI_SILU_MUL, self.z,
+                                                         self.z_scales, workspace=self.gemm_workspace,
+                                                         w13_layout=lay, bind=True)))
+        else:
+            st.append(("gemm_w13", moe_grouped_gemm_w13(self.buf, self.buf_scales, w, self.w13_scales,
+                                                         self.counts, self.offsets, MOE_EPI_STORE_G, self.g,
+                                                         workspace=self.gemm_workspace, w13_layout=lay,
+                                                         bind=True)))
+            st.append(("silu_mul", moe_silu_mul(self.g, self.counts, self.offsets, self.z, self.z_scales,
+                                                bind=True)))
+        st += [
+            ("gemm_w2", moe_grouped_gemm_w2(self.z, self.z_scales, self.w2, self.w2_scales, self.counts,
+                                            self.offsets, self.out, workspace=self.gemm_workspace,
+                                            bind=True)),
+            ("combine", moe_combine(self.out, self.slot_of, topk_weights, self.y, bind=True)),
+        ]
+        return st
+
     def forward(self, x, topk_ids, topk_weights):
         """The whole path on the current stream; returns y [T,H] (no sync)."""
         self.layout(topk_ids)
