@@ -41,6 +41,9 @@ def parse():
                     help="omit the oracle timing (profiling runs)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one plain device copy of this size first (counter calibration)")
+    ap.add_argument("--extra-workloads", default="decode_fp8,skewed_bf16",
+                    help="comma-separated workloads also timed after the main one (stage and "
+                         "kernel times only); empty for none")
     return ap.parse_args()
 
 
@@ -72,12 +75,15 @@ def recorded_traffic(workload: str):
     return float(kv["gemm_w13_bytes_per_launch"])
 
 
-def algorithmic_work(cfg, counts):
+def algorithmic_work(cfg, counts, tok_local=None):
     """Bytes and FLOPs each kernel must move / compute at minimum.
 
     Weights of experts with at least one row are read once; every valid row
     of A, Z and the expert output is read or written once; padding rows do
-    not count."""
+    not count ("SGLang、NCCL 与 MoE EP" §2.3.7: the valid rows' bytes, not the
+    receive area's, are the traffic).  Permute reads each token with a local
+    route once (tok_local of them) and writes its rows; combine reads every
+    row and writes every token."""
     rows = int(counts.sum())
     active = int((counts > 0).sum())
     H, I = cfg.H, cfg.I
@@ -92,14 +98,19 @@ def algorithmic_work(cfg, counts):
     a_bytes = rows * H * ab + (rows * (H // 128) * 4 if fp8 else 0)
     z_bytes = rows * I * zb + (rows * (I // 128) * 4 if fp8 else 0)
     out_bytes = rows * H * ob
-    return {
+    work = {
         "rows": rows,
+        "a_bytes": a_bytes,
         "w13_bytes": w13 + a_bytes + z_bytes,
         "w13_flops": 2.0 * rows * H * 2 * I,
         "w2_bytes": w2 + z_bytes + out_bytes,
         "w2_flops": 2.0 * rows * I * H,
         "gemm_flops": 6.0 * H * I * rows,
     }
+    if tok_local is not None:
+        work["permute_bytes"] = tok_local * H * xb + a_bytes + cfg.T * cfg.K * 4
+        work["combine_bytes"] = out_bytes + cfg.T * H * ob + cfg.T * cfg.K * 8
+    return work
 
 
 def cpu_baseline(wl, n_tokens):
@@ -107,7 +118,7 @@ def cpu_baseline(wl, n_tokens):
     from threadpoolctl import threadpool_info, threadpool_limits
     from oracle import moe
 
-    cores = min(len(os.sched_getaffinity(0)), 16)
+    cores = len(os.sched_getaffinity(0))
     tokens = np.arange(min(n_tokens, wl.cfg.T))
     with threadpool_limits(limits=cores):
         blas = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
@@ -239,26 +250,17 @@ def backward_timing(cfg, layer, x, ids, w, steps, dev):
     return res
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU's share of the MoE layer; --gpus {args.gpus} is not "
-              "supported (the multi-GPU expert-parallel exchange is not implemented)",
-              file=sys.stderr)
-        sys.exit(2)
-
+def build_layer(cfg, dev):
+    """Seeded inputs of a workload, uploaded, and a layer holding its weights."""
     import torch
 
-    import combine_top_expert_amd  # noqa: F401  (fails loudly without the HIP library)
     from combine_top_expert_amd.pipeline import LayerShape, MoELayer
-    from workloads import get_config, make_workload
+    from workloads import make_workload
 
-    cfg = get_config(args.workload)
     print(f"[bench] generating {cfg.name} inputs", file=sys.stderr, flush=True)
     wl = make_workload(cfg)
     shape = LayerShape(T=cfg.T, K=cfg.K, E=cfg.E, expert_begin=cfg.expert_begin, L=cfg.L, H=cfg.H,
                        I=cfg.I, R=cfg.R, act=cfg.act, wdt=cfg.wdt)
-    dev = torch.device("cuda:0")
 
     def up(a, bf16=False):
         t = torch.from_numpy(np.ascontiguousarray(a))
@@ -272,6 +274,93 @@ def main():
     ids = up(wl.ids)
     w = up(wl.weights)
     torch.cuda.synchronize()
+    # each launch marshalled once: a step costs a few microseconds of host time
+    bound = layer.bind_forward(x, ids, w)
+    stages = [n for n, _ in bound]
+    fns = [f for _, f in bound]
+    return wl, layer, x, ids, w, stages, fns
+
+
+def stage_pass(stages, fns, steps, stream):
+    """Another ``steps`` whole steps with an event between stages: medians
+    (and p10/p90) per stage, median step total."""
+    import torch
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for s in range(steps):
+        ev[s][0].record(stream)
+        for i, f in enumerate(fns):
+            f()
+            ev[s][i + 1].record(stream)
+    torch.cuda.synchronize()
+    per = np.array([[ev[s][i].elapsed_time(ev[s][i + 1]) for i in range(len(stages))]
+                    for s in range(steps)]) * 1e3                       # us
+    stage_us = {k: float(np.median(per[:, i])) for i, k in enumerate(stages)}
+    p10_90 = {k: [float(np.percentile(per[:, i], 10)), float(np.percentile(per[:, i], 90))]
+              for i, k in enumerate(stages)}
+    return stage_us, p10_90, float(np.median(per.sum(axis=1)))
+
+
+def roofline(work, prefix, us, peak_tf):
+    """HBM or MFMA roofline of one GEMM call from its algorithmic bytes and
+    flops and its measured duration: the bound is whichever resource takes
+    longer at its peak."""
+    b, f = work[prefix + "_bytes"], work[prefix + "_flops"]
+    if b / (HBM_PEAK_GBS * 1e9) >= f / (peak_tf * 1e12):
+        r = {"bound": "hbm", "achieved": b / (us * 1e-6) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    else:
+        r = {"bound": "mfma", "achieved": f / (us * 1e-6) / 1e12, "peak": peak_tf, "unit": "TFLOP/s"}
+    r["frac"] = r["achieved"] / r["peak"]
+    r["avg_us"] = us
+    r["algorithmic_bytes"] = b
+    r["algorithmic_flops"] = f
+    r["mfma_frac"] = f / (us * 1e-6) / 1e12 / peak_tf
+    r["hbm_frac"] = b / (us * 1e-6) / 1e9 / HBM_PEAK_GBS
+    return r
+
+
+def workload_summary(cfg, layer, stages, fns, steps, stream):
+    """Per-stage medians (a pass of whole steps with an event between
+    stages) and the derived rates of one workload."""
+    stage_us, p10_90, gpu_us = stage_pass(stages, fns, steps, stream)
+    slot = layer.slot_of.cpu().numpy()
+    counts = layer.counts.cpu().numpy()
+    work = algorithmic_work(cfg, counts, int((slot >= 0).any(axis=1).sum()))
+    loop = stage_us
+    peak = MFMA_PEAK_TFLOPS[cfg.wdt]
+    gemm_us = loop["gemm_w13"] + loop["gemm_w2"]
+    return {
+        "config": {"workload": cfg.name, "T": cfg.T, "K": cfg.K, "E": cfg.E, "L": cfg.L, "H": cfg.H,
+                   "I": cfg.I, "R": cfg.R, "rows": work["rows"], "weights": cfg.wdt},
+        "rows_per_s_stage_sum": work["rows"] / (gpu_us * 1e-6),
+        "stage_us": stage_us, "stage_p10_p90_us": p10_90, "stage_sum_us": gpu_us,
+        "gemm_tflops": work["gemm_flops"] / (gemm_us * 1e-6) / 1e12,
+        "gemm_mfma_frac": work["gemm_flops"] / (gemm_us * 1e-6) / 1e12 / peak,
+        "w13": roofline(work, "w13", loop["gemm_w13"], peak),
+        "w2": roofline(work, "w2", loop["gemm_w2"], peak),
+        "permute_gbs": work["permute_bytes"] / (loop["permute"] * 1e-6) / 1e9,
+        "combine_gbs": work["combine_bytes"] / (loop["combine"] * 1e-6) / 1e9,
+        "permute_bytes": work["permute_bytes"], "combine_bytes": work["combine_bytes"],
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU's share of the MoE layer; --gpus {args.gpus} is not "
+              "supported (the multi-GPU expert-parallel exchange is not implemented)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import combine_top_expert_amd  # noqa: F401  (fails loudly without the HIP library)
+    from workloads import get_config
+
+    cfg = get_config(args.workload)
+    dev = torch.device("cuda:0")
+    wl, layer, x, ids, w, stages, fns = build_layer(cfg, dev)
 
     if args.copy_calibration_mib:
         n = args.copy_calibration_mib << 20
@@ -281,9 +370,6 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    stages = ["layout", "permute", "gemm_w13", "gemm_w2", "combine"]
-    fns = [lambda: layer.layout(ids), lambda: layer.permute(x), layer.gemm_w13, layer.gemm_w2,
-           lambda: layer.combine(w)]
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         for f in fns:
@@ -291,72 +377,44 @@ def main():
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream(dev)
-    # Timed region: K whole steps.  The only events in it are the two around
-    # the gate/up GEMM (the roofline's kernel); an event between every stage
-    # costs a few microseconds of GPU time each, so the per-stage breakdown
-    # comes from a separate pass below.
-    ev_w13 = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(args.steps)]
+    # Timed region: exactly K whole steps.  The only events in it are the two
+    # around each gate/up GEMM call (the roofline's kernel).  The launches are
+    # pre-marshalled, so the host stays ahead of the device and each event
+    # pair brackets the GEMM call alone.
+    i13 = stages.index("gemm_w13")
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for s in range(args.steps):
-        fns[0]()
-        fns[1]()
-        ev_w13[s][0].record(stream)
-        fns[2]()
-        ev_w13[s][1].record(stream)
-        fns[3]()
-        fns[4]()
+    for s_ in range(args.steps):
+        for i, f in enumerate(fns):
+            if i == i13:
+                ev[s_][0].record(stream)
+                f()
+                ev[s_][1].record(stream)
+            else:
+                f()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     step_ms = wall * 1e3 / args.steps                 # whole-job clock, host included
-    w13_launch_us = [a.elapsed_time(b) * 1e3 for a, b in ev_w13]
-
-    # Per-stage breakdown: another K steps with an event between stages.
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    for s in range(args.steps):
-        ev[s][0].record(stream)
-        for i, f in enumerate(fns):
-            f()
-            ev[s][i + 1].record(stream)
-    torch.cuda.synchronize()
-    per = np.array([[ev[s][i].elapsed_time(ev[s][i + 1]) for i in range(len(stages))]
-                    for s in range(args.steps)])                      # ms
-    gpu_ms = float(np.median(per.sum(axis=1)))        # sum of stage events, median step
+    w13_us = [a.elapsed_time(b) * 1e3 for a, b in ev]
     st = layer.dev_status.cpu().numpy()
     if st[0] != 0:
         raise RuntimeError(f"dispatch layout flagged {st}")
 
+    # After the timed region: per-stage breakdown (events between stages).
+    summ = workload_summary(cfg, layer, stages, fns, args.steps, stream)
     counts = layer.counts.cpu().numpy()
     work = algorithmic_work(cfg, counts)
-    stage_us = {k: float(np.median(per[:, i]) * 1e3) for i, k in enumerate(stages)}
-    stage_p10_p90 = {k: [float(np.percentile(per[:, i], 10) * 1e3), float(np.percentile(per[:, i], 90) * 1e3)]
-                     for i, k in enumerate(stages)}
-    gemm_us = stage_us["gemm_w13"] + stage_us["gemm_w2"]
     peak_tf = MFMA_PEAK_TFLOPS[cfg.wdt]
-    gemm_tflops = work["gemm_flops"] / (gemm_us * 1e-6) / 1e12
-
-    # dominant kernel: the gate/up GEMM (two thirds of the FLOPs), its
-    # average launch duration over the timed region
-    w13_us = float(np.mean(w13_launch_us))
-    t_hbm = work["w13_bytes"] / (HBM_PEAK_GBS * 1e9)
-    t_mfma = work["w13_flops"] / (peak_tf * 1e12)
-    if t_hbm >= t_mfma:
-        ach = work["w13_bytes"] / (w13_us * 1e-6) / 1e9
-        roof = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
-    else:
-        ach = work["w13_flops"] / (w13_us * 1e-6) / 1e12
-        roof = {"bound": "mfma", "achieved": ach, "peak": peak_tf, "unit": "TFLOP/s"}
-    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof = roofline(work, "w13", float(np.mean(w13_us)), peak_tf)
+    roof["p10_p90_us"] = [float(np.percentile(w13_us, 10)), float(np.percentile(w13_us, 90))]
     roof["traffic"] = recorded_traffic(cfg.name)
-    roof["kernel"] = "grouped_gemm_kernel (moe_grouped_gemm_w13, fused SiLU*up, FP8 Z)"
-    roof["avg_us"] = w13_us
-    roof["p10_p90_us"] = [float(np.percentile(w13_launch_us, 10)), float(np.percentile(w13_launch_us, 90))]
-    roof["algorithmic_bytes"] = work["w13_bytes"]
-    roof["algorithmic_flops"] = work["w13_flops"]
-    roof["mfma_frac"] = work["w13_flops"] / (w13_us * 1e-6) / 1e12 / peak_tf
+    roof["kernel"] = ("grouped_gemm_kernel (moe_grouped_gemm_w13, fused SiLU*up, FP8 Z; the call's "
+                      "K-split piece reduce included when it runs)")
+    roof["timing"] = ("mean over the timed steps of HIP events recorded right before and after the "
+                      "gate/up GEMM call on the kernels' stream")
 
     out = {
         "metric": METRIC,
@@ -366,9 +424,9 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": step_ms,
-        "gpu_ms_per_step": gpu_ms,
-        "stage_timing": "stage_us and gpu_ms_per_step: medians of a separate pass of the same "
-                        "number of steps with an event between stages",
+        "gpu_ms_per_step": summ["stage_sum_us"] * 1e-3,
+        "stage_timing": "stage_us: medians of a second pass of the same number of steps with an "
+                        "event between stages",
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -377,27 +435,15 @@ def main():
         "config": {"workload": cfg.name, "T": cfg.T, "K": cfg.K, "E": cfg.E, "L": cfg.L,
                    "H": cfg.H, "I": cfg.I, "R": cfg.R, "rows": work["rows"],
                    "act": cfg.act, "weights": cfg.wdt, "seed": cfg.seed},
-        "gemm_tflops": gemm_tflops,
-        "gemm_mfma_frac": gemm_tflops / peak_tf,
-        "stage_us": stage_us,
-        "stage_p10_p90_us": stage_p10_p90,
-        "stage_gbs": {
-            "permute": None, "combine": None,
-        },
+        "gemm_tflops": summ["gemm_tflops"],
+        "gemm_mfma_frac": summ["gemm_mfma_frac"],
+        "stage_us": summ["stage_us"],
+        "stage_p10_p90_us": summ["stage_p10_p90_us"],
+        "stage_gbs": {"permute": summ["permute_gbs"], "combine": summ["combine_gbs"]},
         "roofline": roof,
+        "roofline_w2": summ["w2"],
         "cpu_baseline": None,
     }
-    # permute / combine algorithmic bandwidth
-    slot = layer.slot_of.cpu().numpy()
-    tok_local = int((slot >= 0).any(axis=1).sum())
-    xb = {"bf16": 2, "f32": 4}[cfg.act]
-    ab = {"fp8": 1, "bf16": 2, "f32": 4}[cfg.buf_dt]
-    ob = {"bf16": 2, "f32": 4}[cfg.out_dt]
-    perm_bytes = tok_local * cfg.H * xb + work["rows"] * cfg.H * ab + \
-        (work["rows"] * (cfg.H // 128) * 4 if cfg.buf_dt == "fp8" else 0) + cfg.T * cfg.K * 4
-    comb_bytes = work["rows"] * cfg.H * ob + cfg.T * cfg.H * ob + cfg.T * cfg.K * 8
-    out["stage_gbs"] = {"permute": perm_bytes / (stage_us["permute"] * 1e-6) / 1e9,
-                        "combine": comb_bytes / (stage_us["combine"] * 1e-6) / 1e9}
 
     out["next_rows"] = {}
     if cfg.routing == "softmax":
@@ -405,6 +451,26 @@ def main():
     if cfg.wdt != "fp8" and not args.skip_backward:
         print("[bench] backward stages", file=sys.stderr, flush=True)
         out["next_rows"]["backward"] = backward_timing(cfg, layer, x, ids, w, min(args.steps, 20), dev)
+
+    extra = [n for n in args.extra_workloads.split(",") if n and n != cfg.name]
+    if extra:
+        del layer, x, ids, w, fns
+        torch.cuda.empty_cache()
+        out["other_workloads"] = {}
+        for name in extra:
+            ecfg = get_config(name)
+            ewl, elayer, ex, eids, ew, est, efns = build_layer(ecfg, dev)
+            for _ in range(max(args.warmup, 5)):
+                for f in efns:
+                    f()
+            torch.cuda.synchronize()
+            print(f"[bench] {name}: stages and kernel loops", file=sys.stderr, flush=True)
+            out["other_workloads"][name] = workload_summary(ecfg, elayer, est, efns, min(args.steps, 20),
+                                                            stream)
+            del ewl, elayer, ex, eids, ew, efns
+            torch.cuda.empty_cache()
+        torch.cuda.synchronize()
+
     if not args.skip_cpu_baseline:
         print("[bench] cpu baseline (oracle sample)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_sample_tokens)
