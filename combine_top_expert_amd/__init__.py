@@ -23,7 +23,8 @@ __all__ = [
     "moe_status_string", "moe_abi_version", "moe_dispatch_layout_workspace_bytes",
     "moe_grouped_gemm_workspace_bytes", "moe_pack_w13", "MOE_W_ROW_MAJOR", "MOE_W_PACKED",
     "moe_combine_backward", "moe_silu_mul_backward", "moe_permute_backward", "moe_transpose_weights",
-    "moe_grouped_gemm_wgrad", "moe_dispatch_layout", "moe_permute", "moe_grouped_gemm_w13", "moe_silu_mul",
+    "moe_grouped_gemm_wgrad", "moe_dispatch_layout", "moe_dispatch_layout_noalloc",
+    "moe_dispatch_layout_noalloc_max_bytes", "moe_permute", "moe_grouped_gemm_w13", "moe_silu_mul",
     "moe_grouped_gemm_w2", "moe_combine", "moe_router_topk", "dtype_code",
 ]
 
@@ -45,6 +46,8 @@ _SIG = {
     "moe_abi_version": (_i, []),
     "moe_dispatch_layout_workspace_bytes": (_sz, [_i, _i, _i]),
     "moe_dispatch_layout": (_i, [_p, _i, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _sz, _p]),
+    "moe_dispatch_layout_noalloc": (_i, [_p, _i, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p]),
+    "moe_dispatch_layout_noalloc_max_bytes": (_sz, []),
     "moe_permute": (_i, [_p, _i, _i, _i, _i, _p, _i64, _p, _i, _p, _p]),
     "moe_grouped_gemm_w13": (_i, [_p, _i, _p, _p, _i, _p, _i, _p, _p, _i, _i64, _i, _i, _i, _p, _i,
                                   _p, _p, _sz, _p]),
@@ -190,6 +193,30 @@ def moe_dispatch_layout(topk_ids, E_global, expert_begin, L, R, BM, counts, offs
         _i32(row_src, "row_src"), _i32(tile_offsets, "tile_offsets"),
         _i32(dev_status, "dev_status"), _ptr(workspace, "workspace"),
         workspace.numel() * workspace.element_size(), _stream(topk_ids)))
+
+
+def moe_dispatch_layout_noalloc_max_bytes() -> int:
+    return int(lib.moe_dispatch_layout_noalloc_max_bytes())
+
+
+def moe_dispatch_layout_noalloc(topk_ids, E_global, expert_begin, L, R, BM, counts, offsets, slot_of,
+                                row_src, tile_offsets, dev_status, bind=False):
+    """moe_dispatch_layout with the library's per-device scratch in place of
+    a workspace (the C call allocates nothing; see moe_ep.h for the size
+    limit and the sharing rule)."""
+    T, K = topk_ids.shape
+    rows_cap = L * R if R > 0 else T * K
+    _shape(counts, "counts", L)
+    _shape(offsets, "offsets", L + 1)
+    _shape(slot_of, "slot_of", T, K)
+    _shape(row_src, "row_src", rows_cap)
+    _shape(tile_offsets, "tile_offsets", L + 1)
+    _shape(dev_status, "dev_status", 2)
+    return _run("moe_dispatch_layout_noalloc", bind, (
+        _i32(topk_ids, "topk_ids"), T, K, E_global, expert_begin, L, R, BM,
+        _i32(counts, "counts"), _i32(offsets, "offsets"), _i32(slot_of, "slot_of"),
+        _i32(row_src, "row_src"), _i32(tile_offsets, "tile_offsets"),
+        _i32(dev_status, "dev_status"), _stream(topk_ids)))
 
 
 def moe_permute(x, slot_of, buf, buf_scales=None, bind=False):

@@ -25,6 +25,8 @@
 // block's share; two (count, then scan fused into place: each block reads
 // the whole histogram table) while that table is small; otherwise three.
 
+#include <mutex>
+
 #include "moe_common.h"
 
 namespace {
@@ -490,12 +492,12 @@ extern "C" size_t moe_dispatch_layout_workspace_bytes(int T, int K, int L) {
   return static_cast<size_t>((nblk * L + nblk + 64) * sizeof(int32_t));
 }
 
-extern "C" moe_status moe_dispatch_layout(const int32_t* topk_ids, int T, int K, int E_global,
-                                          int expert_begin, int L, int R, int BM,
-                                          int32_t* counts, int32_t* offsets, int32_t* slot_of,
-                                          int32_t* row_src, int32_t* tile_offsets,
-                                          int32_t* dev_status, void* workspace,
-                                          size_t workspace_bytes, hipStream_t stream) {
+namespace {
+
+moe_status dispatch_layout(const int32_t* topk_ids, int T, int K, int E_global, int expert_begin, int L,
+                           int R, int BM, int32_t* counts, int32_t* offsets, int32_t* slot_of,
+                           int32_t* row_src, int32_t* tile_offsets, int32_t* dev_status, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream) {
   MOE_CHECK(T >= 0 && K > 0 && E_global > 0 && L >= 1 && L <= kMaxL && R >= 0 && BM > 0 &&
                 expert_begin >= 0 && expert_begin + L <= E_global,
             MOE_ERR_INVALID_ARG);
@@ -548,4 +550,63 @@ extern "C" moe_status moe_dispatch_layout(const int32_t* topk_ids, int T, int K,
   }
   MOE_LAUNCH_CHECK();
   return MOE_OK;
+}
+
+// Scratch of the allocation-free entry point: the count pass's per-block
+// histograms, one copy per device for the life of the process.  Host code
+// never passes the symbol itself to a kernel (in host code it is only a
+// stand-in); it passes the device address hipGetSymbolAddress returns.
+constexpr size_t kScratchInts = size_t(1) << 20;                 // 4 MiB
+__device__ __align__(256) int32_t scratch[kScratchInts];
+
+constexpr int kMaxDev = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDev] = {};
+
+// Device address of this device's scratch, looked up once per device (with
+// that device current); null if the runtime refuses.
+void* device_scratch() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" moe_status moe_dispatch_layout(const int32_t* topk_ids, int T, int K, int E_global,
+                                          int expert_begin, int L, int R, int BM,
+                                          int32_t* counts, int32_t* offsets, int32_t* slot_of,
+                                          int32_t* row_src, int32_t* tile_offsets,
+                                          int32_t* dev_status, void* workspace,
+                                          size_t workspace_bytes, hipStream_t stream) {
+  return dispatch_layout(topk_ids, T, K, E_global, expert_begin, L, R, BM, counts, offsets, slot_of,
+                         row_src, tile_offsets, dev_status, workspace, workspace_bytes, stream);
+}
+
+extern "C" size_t moe_dispatch_layout_noalloc_max_bytes(void) { return kScratchInts * sizeof(int32_t); }
+
+extern "C" moe_status moe_dispatch_layout_noalloc(const int32_t* topk_ids, int T, int K, int E_global,
+                                                  int expert_begin, int L, int R, int BM,
+                                                  int32_t* counts, int32_t* offsets, int32_t* slot_of,
+                                                  int32_t* row_src, int32_t* tile_offsets,
+                                                  int32_t* dev_status, hipStream_t stream) {
+  // argument errors first, exactly as the workspace entry point reports them
+  MOE_CHECK(T >= 0 && K > 0 && E_global > 0 && L >= 1 && L <= kMaxL && R >= 0 && BM > 0 &&
+                expert_begin >= 0 && expert_begin + L <= E_global,
+            MOE_ERR_INVALID_ARG);
+  MOE_CHECK(static_cast<int64_t>(T) * K <= (int64_t(1) << 30), MOE_ERR_UNSUPPORTED);
+  // the count pass rewrites every histogram entry and flag it uses on every
+  // call, so nothing of a previous call's scratch contents is read
+  MOE_CHECK(moe_dispatch_layout_workspace_bytes(T, K, L) <= kScratchInts * sizeof(int32_t),
+            MOE_ERR_WORKSPACE);
+  void* ws = device_scratch();
+  if (ws == nullptr) return MOE_ERR_HIP;
+  return dispatch_layout(topk_ids, T, K, E_global, expert_begin, L, R, BM, counts, offsets, slot_of,
+                         row_src, tile_offsets, dev_status, ws, kScratchInts * sizeof(int32_t), stream);
 }

@@ -81,7 +81,7 @@ const char* moe_status_string(int status);
 
 /* ABI version; bumped on any signature change or added entry point (2: moe_router_topk;
  * 3: GEMM workspace for the K-split last round; 4: moe_pack_w13 and the W13 layout;
- * 5: the backward entry points; 6: moe_grouped_gemm_wgrad). */
+ * 5: the backward entry points; 6: moe_grouped_gemm_wgrad; 7: moe_dispatch_layout_noalloc). */
 int moe_abi_version(void);
 
 /* Bytes of device workspace moe_dispatch_layout needs for (T, K, L). */
@@ -121,6 +121,31 @@ moe_status moe_dispatch_layout(const int32_t* topk_ids, int T, int K, int E_glob
                                int32_t* counts, int32_t* offsets, int32_t* slot_of,
                                int32_t* row_src, int32_t* tile_offsets, int32_t* dev_status,
                                void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * moe_dispatch_layout_noalloc -- moe_dispatch_layout without a caller
+ * workspace, for callers that cannot allocate device memory (code under HIP
+ * graph capture, serving loops, harnesses that forbid hipMalloc).  Same
+ * arguments, results and errors as moe_dispatch_layout; the count pass's
+ * per-block histograms go to a scratch array of the library instead, one per
+ * device, held until the process ends.  The call allocates nothing.
+ *   Limit: moe_dispatch_layout_workspace_bytes(T, K, L) must not exceed
+ *   moe_dispatch_layout_noalloc_max_bytes() (4 MiB: up to about 32 million
+ *   routes T*K at L = 32, 4 million at L = 256); larger sizes return
+ *   MOE_ERR_WORKSPACE before anything is enqueued.  MOE_ERR_HIP if the runtime cannot resolve the scratch address.
+ *   Every call on a device shares that device's scratch: calls that overlap
+ *   in time on one device (other streams, other host threads) race and must
+ *   be ordered by the caller.  Each call rewrites every scratch entry it
+ *   reads, so nothing of an earlier call carries over.
+ */
+moe_status moe_dispatch_layout_noalloc(const int32_t* topk_ids, int T, int K, int E_global,
+                                       int expert_begin, int L, int R, int BM,
+                                       int32_t* counts, int32_t* offsets, int32_t* slot_of,
+                                       int32_t* row_src, int32_t* tile_offsets, int32_t* dev_status,
+                                       hipStream_t stream);
+
+/* Largest workspace (bytes) moe_dispatch_layout_noalloc can stand in for. */
+size_t moe_dispatch_layout_noalloc_max_bytes(void);
 
 /*
  * moe_permute -- fill the expert-major buffer from token rows.

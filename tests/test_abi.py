@@ -37,9 +37,10 @@ def test_header_declares_the_entry_points():
                  "moe_grouped_gemm_w2", "moe_combine", "moe_router_topk",
                  "moe_grouped_gemm_workspace_bytes", "moe_pack_w13", "moe_combine_backward",
                  "moe_silu_mul_backward", "moe_permute_backward", "moe_transpose_weights",
-                 "moe_grouped_gemm_wgrad"]:
+                 "moe_grouped_gemm_wgrad", "moe_dispatch_layout_noalloc",
+                 "moe_dispatch_layout_noalloc_max_bytes"]:
         assert name in fns
-    assert len(fns) == 17
+    assert len(fns) == 19
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -58,7 +59,7 @@ def test_status_strings_and_version(lib):
     assert lib.moe_status_string(0) == b"MOE_OK"
     assert lib.moe_status_string(-2) == b"MOE_ERR_UNSUPPORTED"
     assert lib.moe_status_string(12345) == b"MOE_ERR_UNKNOWN"
-    assert lib.moe_abi_version() == 6
+    assert lib.moe_abi_version() == 7
 
 
 def test_workspace_bytes(lib):
@@ -179,7 +180,7 @@ def test_python_binding_loads_and_matches_header(lib):
     import combine_top_expert_amd as ep
     for name in declared_functions():
         assert callable(getattr(ep, name)), name
-    assert ep.moe_abi_version() == 6
+    assert ep.moe_abi_version() == 7
     assert ep.moe_status_string(-1) == "MOE_ERR_INVALID_ARG"
 
 
@@ -256,3 +257,30 @@ def test_backward_argument_errors(lib):
     assert wg(P(258), A, 1, A, A, 4, 64, 128, 128, A, None) == INVALID                  # misaligned b
     assert wg(A, None, 1, A, A, 4, 64, 128, 128, A, None) == INVALID                    # no a
     assert wg(A, A, 1, A, A, 4, 64, 128, 128, P(260), None) == INVALID                  # misaligned c
+
+
+def test_layout_noalloc_argument_errors(lib):
+    """The allocation-free layout reports argument errors like the workspace
+    entry point and rejects sizes beyond its scratch before any device call."""
+    f = lib.moe_dispatch_layout_noalloc
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_void_p] + [ctypes.c_int] * 7 + [ctypes.c_void_p] * 7
+    mx = lib.moe_dispatch_layout_noalloc_max_bytes
+    mx.restype = ctypes.c_size_t
+    ws = lib.moe_dispatch_layout_workspace_bytes
+    ws.restype = ctypes.c_size_t
+    ws.argtypes = [ctypes.c_int] * 3
+    assert mx() == 4 << 20
+    p = [P()] * 6
+
+    def call(T=64, K=8, E=256, e0=0, L=32, R=128, BM=128):
+        return f(P(), T, K, E, e0, L, R, BM, *p, None)
+
+    assert call(L=0) == INVALID
+    assert call(K=0) == INVALID
+    assert call(e0=250) == INVALID                   # owned range past E_global
+    assert call(T=1 << 28, K=8) == UNSUPPORTED       # more than 2^30 routes
+    # T*K routes need ceil(T*K/1024) * (L + 1) + 64 ints of histogram table
+    assert ws(1 << 20, 8, 1024) > mx()
+    assert call(T=1 << 20, K=8, E=1024, L=1024) == WORKSPACE
+    assert ws(1 << 21, 8, 32) <= mx()                # 16M routes at L = 32 fit
