@@ -85,7 +85,8 @@ constexpr int kRsrcWord3 = 0x00020000;             // raw buffer: 32-bit data fo
 static_assert(STAGE % 16 == 0, "stage slots must stay 16-byte aligned");
 
 enum Dt { DT_F32 = 0, DT_BF16 = 1, DT_FP8 = 2 };
-enum Epi { EPI_STORE_F32 = 0, EPI_STORE_BF16 = 1, EPI_SILU_F32 = 2, EPI_SILU_BF16 = 3, EPI_SILU_FP8 = 4 };
+enum Epi { EPI_STORE_F32 = 0, EPI_STORE_BF16 = 1, EPI_SILU_F32 = 2, EPI_SILU_BF16 = 3, EPI_SILU_FP8 = 4,
+           EPI_SCATTER_F32 = 5 };
 
 struct GemmArgs {
   const uint8_t* A;      // [rows_cap, K] elements
@@ -107,6 +108,11 @@ struct GemmArgs {
   float* part;           // K-split partial sums [grid][BM][2*BH] fp32, or null (no split)
   int* desc;             // [grid][kDescInts]: the K-split piece each workgroup ran
   int w_packed;          // W in the packed layout (moe_pack_w13), else [L, N, K]
+  // EPI_SCATTER_F32 (down GEMM adding weighted rows into token sums):
+  const int32_t* row_src;    // [rows_cap]: t * topk + k of each valid row
+  const float* route_w;      // [T, topk] router weights
+  float* y_acc;              // [T, ldo] fp32 token sums
+  int topk;
 };
 
 constexpr int kDescInts = 16;
@@ -615,6 +621,28 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs p) {
           for (int j = 0; j < 2; ++j)
             *reinterpret_cast<v4f*>(pp + (mrow + 16 * i) * (2 * BH) + h * BH + ncol + 16 * j) = acc[i][h][j];
       }
+    } else if constexpr (EPI == EPI_SCATTER_F32) {
+      // out[q, n] * w[t, k] added into y_acc[t, n] (t, k the row's route):
+      // the combine's weighted sum made in the down GEMM's epilogue, summed
+      // in whatever order the atomic adds arrive
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = mrow + 16 * i;
+        if (row >= rows_valid) continue;
+        const int src = p.row_src[row0 + row];
+        const float w = p.route_w[src];
+        float* yrow = p.y_acc + static_cast<int64_t>(src / p.topk) * p.ldo;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          if (h == 1 && !half1) continue;
+          const int ncol0 = n0 + h * p.half_stride;
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              unsafeAtomicAdd(yrow + ncol0 + ncol + 16 * j + r, acc[i][h][j][r] * w);
+        }
+      }
     } else if constexpr (EPI == EPI_STORE_F32 || EPI == EPI_STORE_BF16) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
@@ -726,6 +754,7 @@ constexpr int kReduceRows = 2 * (kReduceThreads / MOE_WAVE);   // rows per block
 
 template <int EPI>
 __global__ __launch_bounds__(kReduceThreads) void gemm_piece_reduce_kernel(GemmArgs p) {
+  if constexpr (EPI == EPI_SCATTER_F32) return;     // never split: launched without a workspace
   const int* d = p.desc + static_cast<int64_t>(blockIdx.x) * kDescInts;
   if (d[0] == 0 || d[2] != 0) return;              // no piece, or not a tile's first one
   const int S = d[1], bstride = d[3], rows_valid = d[4], n0 = d[5], nb = d[6];
@@ -987,6 +1016,86 @@ extern "C" moe_status moe_grouped_gemm_w2(const void* z, moe_dtype z_dt, const f
   if (ws_st != MOE_OK) return ws_st;
   if (out_dt == MOE_F32) return dispatch_dt<EPI_STORE_F32>(z_dt, g, mt, stream);
   return dispatch_dt<EPI_STORE_BF16>(z_dt, g, mt, stream);
+}
+
+namespace {
+
+// y_acc = 0, 16 bytes per thread, grid-stride (a fill kernel rather than a
+// memset node, so the call can be captured in a graph)
+__global__ __launch_bounds__(256) void zero_f32_kernel(float* __restrict__ p, int64_t n4) {
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n4;
+       i += static_cast<int64_t>(gridDim.x) * 256)
+    reinterpret_cast<float4*>(p)[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
+// y = y_acc rounded to bf16 (RNE) or copied (fp32), 4 values per thread
+__global__ __launch_bounds__(256) void finish_rows_kernel(const float* __restrict__ acc, int64_t n4, void* y,
+                                                         int y_bf16) {
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n4;
+       i += static_cast<int64_t>(gridDim.x) * 256) {
+    const float4 v = reinterpret_cast<const float4*>(acc)[i];
+    if (y_bf16) {
+      reinterpret_cast<uint2*>(y)[i] = make_uint2(
+          static_cast<uint32_t>(moe::f32_to_bf16(v.x)) | (static_cast<uint32_t>(moe::f32_to_bf16(v.y)) << 16),
+          static_cast<uint32_t>(moe::f32_to_bf16(v.z)) | (static_cast<uint32_t>(moe::f32_to_bf16(v.w)) << 16));
+    } else {
+      reinterpret_cast<float4*>(y)[i] = v;
+    }
+  }
+}
+
+}  // namespace
+
+extern "C" moe_status moe_grouped_gemm_w2_combine(const void* z, moe_dtype z_dt, const float* z_scales,
+                                                  const void* w2, moe_dtype w_dt, const float* w2_scales,
+                                                  const int32_t* counts, const int32_t* offsets, int L,
+                                                  int64_t rows_cap, int H, int I, const int32_t* row_src,
+                                                  const float* topk_weights, int T, int K, float* y_acc,
+                                                  void* y, moe_dtype y_dt, hipStream_t stream) {
+  MOE_CHECK(L >= 1 && L <= kMaxL && rows_cap >= 0 && H > 0 && I > 0 && T >= 0 && K > 0, MOE_ERR_INVALID_ARG);
+  MOE_CHECK(moe_host::valid_dtype(z_dt) && moe_host::valid_dtype(w_dt) && moe_host::valid_dtype(y_dt),
+            MOE_ERR_INVALID_ARG);
+  MOE_CHECK(z_dt == w_dt, MOE_ERR_UNSUPPORTED);
+  MOE_CHECK(H % 128 == 0 && I % 128 == 0, MOE_ERR_UNSUPPORTED);
+  MOE_CHECK(y_dt == MOE_F32 || y_dt == MOE_BF16, MOE_ERR_UNSUPPORTED);
+  MOE_CHECK(offsets_fit(static_cast<int64_t>(I) * moe_host::elem_bytes(z_dt), H, rows_cap),
+            MOE_ERR_UNSUPPORTED);
+  MOE_CHECK(z_dt != MOE_FP8_E4M3 || I <= 128 * 128, MOE_ERR_UNSUPPORTED);
+  if (T == 0) return MOE_OK;
+  MOE_CHECK(y_acc && y, MOE_ERR_INVALID_ARG);
+  MOE_CHECK(((reinterpret_cast<uintptr_t>(y_acc) | reinterpret_cast<uintptr_t>(y)) & 15) == 0, MOE_ERR_INVALID_ARG);
+  const int64_t n4 = static_cast<int64_t>(T) * H / 4;
+  const int fill_grid = static_cast<int>(std::min<int64_t>((n4 + 255) / 256, 8192));
+  zero_f32_kernel<<<fill_grid, 256, 0, stream>>>(y_acc, n4);
+  MOE_LAUNCH_CHECK();
+  if (rows_cap > 0) {
+    MOE_CHECK(z && w2 && counts && offsets && row_src && topk_weights, MOE_ERR_INVALID_ARG);
+    MOE_CHECK(z_dt != MOE_FP8_E4M3 || (z_scales && w2_scales), MOE_ERR_INVALID_ARG);
+    GemmArgs g{};
+    g.A = static_cast<const uint8_t*>(z);
+    g.As = z_scales;
+    g.W = static_cast<const uint8_t*>(w2);
+    g.Ws = w2_scales;
+    g.counts = counts;
+    g.offsets = offsets;
+    g.L = L;
+    g.K = I;
+    g.N = H;
+    g.nb_count = (H + 2 * BH - 1) / (2 * BH);
+    g.nb_stride = 2 * BH;
+    g.half_stride = BH;
+    g.rows_cap = rows_cap;
+    g.ldo = H;
+    g.row_src = row_src;
+    g.route_w = topk_weights;
+    g.y_acc = y_acc;
+    g.topk = K;
+    const moe_status st = dispatch_dt<EPI_SCATTER_F32>(z_dt, g, max_row_tiles(rows_cap, L), stream);
+    if (st != MOE_OK) return st;
+  }
+  finish_rows_kernel<<<fill_grid, 256, 0, stream>>>(y_acc, n4, y, y_dt == MOE_BF16 ? 1 : 0);
+  MOE_LAUNCH_CHECK();
+  return MOE_OK;
 }
 
 extern "C" size_t moe_grouped_gemm_workspace_bytes(void) {
