@@ -165,8 +165,9 @@ def router_timing(cfg, steps, dev):
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) * 1e3 / n
     nbytes = cfg.T * cfg.E * 4 + cfg.E * 4 + cfg.T * cfg.K * 8
-    return {"us": us, "bytes": nbytes, "gbs": nbytes / (us * 1e-6) / 1e9,
-            "shape": {"T": cfg.T, "E": cfg.E, "K": cfg.K, "bias": cfg.bias}}
+    res = {"us": us, "bytes": nbytes, "gbs": nbytes / (us * 1e-6) / 1e9,
+           "shape": {"T": cfg.T, "E": cfg.E, "K": cfg.K, "bias": cfg.bias}}
+    return res
 
 
 def _time_stages(stages, steps, dev):
@@ -320,9 +321,37 @@ def roofline(work, prefix, us, peak_tf):
     return r
 
 
-def workload_summary(cfg, layer, stages, fns, steps, stream):
+def w2_combine_us(layer, topk_weights, steps, stream):
+    """The down GEMM with the combine in its epilogue
+    (moe_grouped_gemm_w2_combine: zero fill, GEMM with weighted atomic adds,
+    rounding pass) timed like a stage: median of ``steps`` calls, each between
+    two events, after the layer's forward has produced Z."""
+    import torch
+
+    import combine_top_expert_amd as ep
+
+    s = layer.shape
+    y_acc = torch.empty(s.T, s.H, dtype=torch.float32, device=layer.y.device)
+    y = torch.empty_like(layer.y)
+    f = ep.moe_grouped_gemm_w2_combine(layer.z, layer.z_scales, layer.w2, layer.w2_scales, layer.counts,
+                                       layer.offsets, layer.row_src, topk_weights, y_acc, y, bind=True)
+    for _ in range(3):
+        f()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for a, b in ev:
+        a.record(stream)
+        f()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return float(np.median([a.elapsed_time(b) * 1e3 for a, b in ev]))
+
+
+def workload_summary(cfg, layer, stages, fns, steps, stream, topk_weights=None):
     """Per-stage medians (a pass of whole steps with an event between
-    stages) and the derived rates of one workload."""
+    stages) and the derived rates of one workload; with topk_weights, also
+    the fused down GEMM + combine alternative against the two stages it
+    replaces."""
     stage_us, p10_90, gpu_us = stage_pass(stages, fns, steps, stream)
     slot = layer.slot_of.cpu().numpy()
     counts = layer.counts.cpu().numpy()
@@ -342,6 +371,9 @@ def workload_summary(cfg, layer, stages, fns, steps, stream):
         "permute_gbs": work["permute_bytes"] / (loop["permute"] * 1e-6) / 1e9,
         "combine_gbs": work["combine_bytes"] / (loop["combine"] * 1e-6) / 1e9,
         "permute_bytes": work["permute_bytes"], "combine_bytes": work["combine_bytes"],
+        **({"w2_combine_fused_us": w2_combine_us(layer, topk_weights, steps, stream),
+            "w2_plus_combine_us": stage_us["gemm_w2"] + stage_us["combine"]}
+           if topk_weights is not None else {}),
     }
 
 
@@ -404,7 +436,7 @@ def main():
         raise RuntimeError(f"dispatch layout flagged {st}")
 
     # After the timed region: per-stage breakdown (events between stages).
-    summ = workload_summary(cfg, layer, stages, fns, args.steps, stream)
+    summ = workload_summary(cfg, layer, stages, fns, args.steps, stream, topk_weights=w)
     counts = layer.counts.cpu().numpy()
     work = algorithmic_work(cfg, counts)
     peak_tf = MFMA_PEAK_TFLOPS[cfg.wdt]
@@ -442,6 +474,8 @@ def main():
         "stage_gbs": {"permute": summ["permute_gbs"], "combine": summ["combine_gbs"]},
         "roofline": roof,
         "roofline_w2": summ["w2"],
+        "w2_combine_fused_us": summ["w2_combine_fused_us"],
+        "w2_plus_combine_us": summ["w2_plus_combine_us"],
         "cpu_baseline": None,
     }
 
@@ -466,7 +500,7 @@ def main():
             torch.cuda.synchronize()
             print(f"[bench] {name}: stages and kernel loops", file=sys.stderr, flush=True)
             out["other_workloads"][name] = workload_summary(ecfg, elayer, est, efns, min(args.steps, 20),
-                                                            stream)
+                                                            stream, topk_weights=ew)
             del ewl, elayer, ex, eids, ew, efns
             torch.cuda.empty_cache()
         torch.cuda.synchronize()

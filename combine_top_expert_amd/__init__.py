@@ -25,7 +25,8 @@ __all__ = [
     "moe_combine_backward", "moe_silu_mul_backward", "moe_permute_backward", "moe_transpose_weights",
     "moe_grouped_gemm_wgrad", "moe_dispatch_layout", "moe_dispatch_layout_noalloc",
     "moe_dispatch_layout_noalloc_max_bytes", "moe_permute", "moe_grouped_gemm_w13", "moe_silu_mul",
-    "moe_grouped_gemm_w2", "moe_combine", "moe_router_topk", "dtype_code",
+    "moe_grouped_gemm_w2", "moe_grouped_gemm_w2_combine", "moe_combine", "moe_router_topk",
+    "dtype_code",
 ]
 
 LIB_PATH = Path(os.environ.get("MOE_EP_LIB", Path(__file__).resolve().parent / "libmoe_ep.so"))
@@ -57,6 +58,8 @@ _SIG = {
     "moe_grouped_gemm_w2": (_i, [_p, _i, _p, _p, _i, _p, _p, _p, _i, _i64, _i, _i, _p, _i, _p, _sz,
                                  _p]),
     "moe_combine": (_i, [_p, _i, _p, _p, _i, _i, _i, _i64, _p, _i, _p]),
+    "moe_grouped_gemm_w2_combine": (_i, [_p, _i, _p, _p, _i, _p, _p, _p, _i, _i64, _i, _i, _p, _p, _i, _i,
+                                         _p, _p, _i, _p]),
     "moe_router_topk": (_i, [_p, _p, _i, _i, _i, _i, _p, _p, _p]),
     "moe_combine_backward": (_i, [_p, _i, _p, _i, _p, _p, _i, _i, _i, _i64, _p, _i, _p, _p]),
     "moe_silu_mul_backward": (_i, [_p, _p, _i, _p, _p, _i, _i64, _i, _p, _i, _p]),
@@ -315,6 +318,33 @@ def moe_grouped_gemm_w2(z, z_scales, w2, w2_scales, counts, offsets, out, worksp
         _ptr(z, "z"), dtype_code(z), _f32(z_scales, "z_scales"), _ptr(w2, "w2"), dtype_code(w2),
         _f32(w2_scales, "w2_scales"), _i32(counts, "counts"), _i32(offsets, "offsets"), L,
         z.shape[0], H, I, _ptr(out, "out"), dtype_code(out), wp, wb, _stream(z)))
+
+
+def moe_grouped_gemm_w2_combine(z, z_scales, w2, w2_scales, counts, offsets, row_src, topk_weights,
+                                y_acc, y, bind=False):
+    """Down GEMM with the combine in its epilogue: z [rows_cap,I], w2 [L,H,I],
+    row_src [rows_cap], topk_weights [T,K] -> y [T,H] (y_acc [T,H] fp32
+    scratch).  Not bit-reproducible (fp32 atomic adds); see moe_ep.h."""
+    L, H, I = w2.shape
+    rows_cap = z.shape[0]
+    T, K = topk_weights.shape
+    _shape(z, "z", rows_cap, I)
+    fp8 = dtype_code(z) == MOE_FP8_E4M3
+    _need(z_scales, "z_scales", fp8)
+    _need(w2_scales, "w2_scales", fp8)
+    if fp8:
+        _shape(z_scales, "z_scales", rows_cap, I // 128)
+        _shape(w2_scales, "w2_scales", L, H // 128, I // 128)
+    _shape(counts, "counts", L)
+    _offsets(offsets, L)
+    _shape(row_src, "row_src", rows_cap)
+    _shape(y_acc, "y_acc", T, H)
+    _shape(y, "y", T, H)
+    return _run("moe_grouped_gemm_w2_combine", bind, (
+        _ptr(z, "z"), dtype_code(z), _f32(z_scales, "z_scales"), _ptr(w2, "w2"), dtype_code(w2),
+        _f32(w2_scales, "w2_scales"), _i32(counts, "counts"), _i32(offsets, "offsets"), L, rows_cap, H, I,
+        _i32(row_src, "row_src"), _f32(topk_weights, "topk_weights"), T, K, _f32(y_acc, "y_acc"),
+        _ptr(y, "y"), dtype_code(y), _stream(y)))
 
 
 def moe_combine(expert_out, slot_of, topk_weights, y, bind=False):

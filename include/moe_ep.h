@@ -81,7 +81,7 @@ const char* moe_status_string(int status);
 
 /* ABI version; bumped on any signature change or added entry point (2: moe_router_topk;
  * 3: GEMM workspace for the K-split last round; 4: moe_pack_w13 and the W13 layout;
- * 5: the backward entry points; 6: moe_grouped_gemm_wgrad; 7: moe_dispatch_layout_noalloc). */
+ * 5: the backward entry points; 6: moe_grouped_gemm_wgrad; 7: moe_dispatch_layout_noalloc; 8: moe_grouped_gemm_w2_combine). */
 int moe_abi_version(void);
 
 /* Bytes of device workspace moe_dispatch_layout needs for (T, K, L). */
@@ -264,6 +264,33 @@ moe_status moe_grouped_gemm_w2(const void* z, moe_dtype z_dt, const float* z_sca
                                int64_t rows_cap, int H, int I,
                                void* out, moe_dtype out_dt,
                                void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * moe_grouped_gemm_w2_combine -- the down GEMM with the combine folded into
+ * its epilogue: y[t] = sum over the rows q of token t of topk_weights[t,k] *
+ * (Z[q] W2[e]^T), with (t,k) = row_src[q] decoded as t*K + k.  The pages
+ * describe the in-kernel weighted reduce on the combine path ("DeepEP
+ * 架构与实现笔记" §9.6) and fusing the necessary conversions into the expert
+ * computation ("SGLang Expert Compute Backend" §2.4, §4.4).  Three kernels on
+ * `stream`: y_acc = 0; the down GEMM, whose epilogue adds w * out[q, n] into
+ * y_acc[t, n] with fp32 atomic adds (the row outputs are not rounded to the
+ * output format and the sum's order is the arrival order, so results are
+ * not bit-reproducible; they stay within the layer's tolerance); y = y_acc
+ * rounded to y_dt.  Tokens without a local route get 0.
+ *   z, z_scales, w2, w2_scales, counts, offsets: as for moe_grouped_gemm_w2
+ *   row_src [rows_cap] from moe_dispatch_layout; topk_weights [T,K] fp32
+ *   y_acc [T,H] fp32 scratch (caller-owned, 16-byte aligned);
+ *   y [T,H] y_dt in {MOE_F32, MOE_BF16} (16-byte aligned)
+ * Measured slower than moe_grouped_gemm_w2 + moe_combine at the shapes here
+ * (see the design notes); kept as the tested alternative.
+ * Limits as moe_grouped_gemm_w2.
+ */
+moe_status moe_grouped_gemm_w2_combine(const void* z, moe_dtype z_dt, const float* z_scales,
+                                       const void* w2, moe_dtype w_dt, const float* w2_scales,
+                                       const int32_t* counts, const int32_t* offsets, int L,
+                                       int64_t rows_cap, int H, int I, const int32_t* row_src,
+                                       const float* topk_weights, int T, int K, float* y_acc,
+                                       void* y, moe_dtype y_dt, hipStream_t stream);
 
 /*
  * moe_combine -- weighted gather-sum back to token order.

@@ -38,9 +38,9 @@ def test_header_declares_the_entry_points():
                  "moe_grouped_gemm_workspace_bytes", "moe_pack_w13", "moe_combine_backward",
                  "moe_silu_mul_backward", "moe_permute_backward", "moe_transpose_weights",
                  "moe_grouped_gemm_wgrad", "moe_dispatch_layout_noalloc",
-                 "moe_dispatch_layout_noalloc_max_bytes"]:
+                 "moe_dispatch_layout_noalloc_max_bytes", "moe_grouped_gemm_w2_combine"]:
         assert name in fns
-    assert len(fns) == 19
+    assert len(fns) == 20
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -59,7 +59,7 @@ def test_status_strings_and_version(lib):
     assert lib.moe_status_string(0) == b"MOE_OK"
     assert lib.moe_status_string(-2) == b"MOE_ERR_UNSUPPORTED"
     assert lib.moe_status_string(12345) == b"MOE_ERR_UNKNOWN"
-    assert lib.moe_abi_version() == 7
+    assert lib.moe_abi_version() == 8
 
 
 def test_workspace_bytes(lib):
@@ -180,7 +180,7 @@ def test_python_binding_loads_and_matches_header(lib):
     import combine_top_expert_amd as ep
     for name in declared_functions():
         assert callable(getattr(ep, name)), name
-    assert ep.moe_abi_version() == 7
+    assert ep.moe_abi_version() == 8
     assert ep.moe_status_string(-1) == "MOE_ERR_INVALID_ARG"
 
 
