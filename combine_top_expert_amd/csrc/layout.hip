@@ -494,10 +494,10 @@ extern "C" size_t moe_dispatch_layout_workspace_bytes(int T, int K, int L) {
 
 namespace {
 
-moe_status dispatch_layout(const int32_t* topk_ids, int T, int K, int E_global, int expert_begin, int L,
-                           int R, int BM, int32_t* counts, int32_t* offsets, int32_t* slot_of,
-                           int32_t* row_src, int32_t* tile_offsets, int32_t* dev_status, void* workspace,
-                           size_t workspace_bytes, hipStream_t stream) {
+// Argument checks and kernel arguments shared by the entry points.
+moe_status make_args(const int32_t* topk_ids, int T, int K, int E_global, int expert_begin, int L, int R, int BM,
+                     int32_t* counts, int32_t* offsets, int32_t* slot_of, int32_t* row_src, int32_t* tile_offsets,
+                     int32_t* dev_status, void* workspace, size_t workspace_bytes, LayoutArgs* out) {
   MOE_CHECK(T >= 0 && K > 0 && E_global > 0 && L >= 1 && L <= kMaxL && R >= 0 && BM > 0 &&
                 expert_begin >= 0 && expert_begin + L <= E_global,
             MOE_ERR_INVALID_ARG);
@@ -528,19 +528,20 @@ moe_status dispatch_layout(const int32_t* topk_ids, int T, int K, int E_global, 
   a.dev_status = dev_status;
   a.ws_hist = static_cast<int32_t*>(workspace);
   a.ws_bad = a.ws_hist + static_cast<int64_t>(a.n_blocks) * L;
+  *out = a;
+  return MOE_OK;
+}
 
-  // at least enough blocks to sweep row_src's padding in a few passes
-  const int64_t fill_blocks = (rows_cap + kThreads * 8 - 1) / (kThreads * 8);
-  const int grid = static_cast<int>(std::max<int64_t>(std::max<int64_t>(a.n_blocks, fill_blocks), 1));
-  if (a.n_blocks <= 1) {
-    // one block's share of routes: a single launch
-    layout_fused_kernel<true><<<grid, kThreads, 0, stream>>>(a);
-    MOE_LAUNCH_CHECK();
-    return MOE_OK;
-  }
-  layout_count_kernel<<<a.n_blocks, kThreads, 0, stream>>>(a);
-  MOE_LAUNCH_CHECK();
-  if (static_cast<int64_t>(a.n_blocks) * L <= kFusedTable) {
+// at least enough blocks to sweep row_src's padding in a few passes
+int place_grid(const LayoutArgs& a) {
+  const int64_t fill_blocks = (a.rows_cap + kThreads * 8 - 1) / (kThreads * 8);
+  return static_cast<int>(std::max<int64_t>(std::max<int64_t>(a.n_blocks, fill_blocks), 1));
+}
+
+// Scan and place after the count pass has filled the histogram table.
+moe_status launch_place(const LayoutArgs& a, hipStream_t stream) {
+  const int grid = place_grid(a);
+  if (static_cast<int64_t>(a.n_blocks) * a.L <= kFusedTable) {
     // every place block reads the whole histogram table itself
     layout_fused_kernel<false><<<grid, kThreads, 0, stream>>>(a);
   } else {
@@ -550,6 +551,25 @@ moe_status dispatch_layout(const int32_t* topk_ids, int T, int K, int E_global, 
   }
   MOE_LAUNCH_CHECK();
   return MOE_OK;
+}
+
+moe_status dispatch_layout(const int32_t* topk_ids, int T, int K, int E_global, int expert_begin, int L,
+                           int R, int BM, int32_t* counts, int32_t* offsets, int32_t* slot_of,
+                           int32_t* row_src, int32_t* tile_offsets, int32_t* dev_status, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream) {
+  LayoutArgs a;
+  const moe_status st = make_args(topk_ids, T, K, E_global, expert_begin, L, R, BM, counts, offsets, slot_of,
+                                  row_src, tile_offsets, dev_status, workspace, workspace_bytes, &a);
+  if (st != MOE_OK) return st;
+  if (a.n_blocks <= 1) {
+    // one block's share of routes: a single launch
+    layout_fused_kernel<true><<<place_grid(a), kThreads, 0, stream>>>(a);
+    MOE_LAUNCH_CHECK();
+    return MOE_OK;
+  }
+  layout_count_kernel<<<a.n_blocks, kThreads, 0, stream>>>(a);
+  MOE_LAUNCH_CHECK();
+  return launch_place(a, stream);
 }
 
 // Scratch of the allocation-free entry point: the count pass's per-block

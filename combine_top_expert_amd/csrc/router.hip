@@ -12,44 +12,16 @@
 // lanes then form exp(v - max) and its sum with wave reductions, and divide.
 
 #include "moe_common.h"
+#include "router_common.h"
 
 namespace {
+
+using namespace moe_router;
 
 constexpr int kThreads = 256;
 constexpr int kTokPerBlock = kThreads / MOE_WAVE;
 constexpr int kMaxE = 1024;
 constexpr int kMaxK = 64;
-
-// order-preserving image of an fp32 value: larger float -> larger key;
-// every NaN maps below -inf, -0 and +0 map together
-__device__ __forceinline__ uint32_t score_key(float v) {
-  if (v != v) return 0u;
-  uint32_t u = __float_as_uint(v == 0.0f ? 0.0f : v);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t k) {
-#pragma unroll
-  for (int d = 1; d < MOE_WAVE; d <<= 1) {
-    const uint32_t lo = __shfl_xor(static_cast<uint32_t>(k), d);
-    const uint32_t hi = __shfl_xor(static_cast<uint32_t>(k >> 32), d);
-    const uint64_t o = (static_cast<uint64_t>(hi) << 32) | lo;
-    k = o > k ? o : k;
-  }
-  return k;
-}
-
-__device__ __forceinline__ float wave_max_f32(float v) {
-#pragma unroll
-  for (int d = 1; d < MOE_WAVE; d <<= 1) v = fmaxf(v, __shfl_xor(v, d));
-  return v;
-}
-
-__device__ __forceinline__ float wave_sum_f32(float v) {
-#pragma unroll
-  for (int d = 1; d < MOE_WAVE; d <<= 1) v += __shfl_xor(v, d);
-  return v;
-}
 
 template <int NPL>   // scores per lane: E <= 64 * NPL
 __global__ __launch_bounds__(kThreads) void router_topk_kernel(const float* __restrict__ logits,
@@ -61,40 +33,12 @@ __global__ __launch_bounds__(kThreads) void router_topk_kernel(const float* __re
   const int t = blockIdx.x * kTokPerBlock + (threadIdx.x >> 6);
   if (t >= T) return;
   const float* row = logits + static_cast<int64_t>(t) * E;
-  uint64_t key[NPL];
-#pragma unroll
-  for (int j = 0; j < NPL; ++j) {
-    const int e = lane + MOE_WAVE * j;
-    key[j] = 0;                                  // absent: below every real entry
-    if (e < E) {
-      const float v = bias ? row[e] + bias[e] : row[e];
-      // low word 0xffffffff - e > 0, so a present entry (even a NaN score,
-      // high word 0) always beats an absent or retired one (key 0)
-      key[j] = (static_cast<uint64_t>(score_key(v)) << 32) | (0xffffffffu - static_cast<uint32_t>(e));
-    }
-  }
-  int my_id = -1;
-  float my_v = 0.0f;
-  for (int k = 0; k < K; ++k) {
-    uint64_t best = 0;
-#pragma unroll
-    for (int j = 0; j < NPL; ++j) best = key[j] > best ? key[j] : best;
-    const uint64_t win = wave_max_u64(best);
-    const int e = static_cast<int>(0xffffffffu - static_cast<uint32_t>(win));
-    // keys are unique (the expert id is part of them): the owner retires it
-#pragma unroll
-    for (int j = 0; j < NPL; ++j) key[j] = key[j] == win ? 0 : key[j];
-    if (lane == k) my_id = e;
-  }
-  // the value entering the weights: the score, or the unbiased logit when
-  // the bias only steers the selection
-  if (lane < K) my_v = (bias && bias_in_weights) ? row[my_id] + bias[my_id] : row[my_id];
-  const float m = wave_max_f32(lane < K ? my_v : -INFINITY);
-  const float p = lane < K ? expf(my_v - m) : 0.0f;
-  const float s = wave_sum_f32(p);
+  int my_id;
+  float my_w;
+  token_topk<NPL>(row, bias, E, K, bias_in_weights, lane, &my_id, &my_w);
   if (lane < K) {
     ids[static_cast<int64_t>(t) * K + lane] = my_id;
-    weights[static_cast<int64_t>(t) * K + lane] = p / s;
+    weights[static_cast<int64_t>(t) * K + lane] = my_w;
   }
 }
 
