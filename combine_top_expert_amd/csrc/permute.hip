@@ -4,18 +4,24 @@
 //
 // A wavefront reads a token's routes once (lane k = route k), reads its row
 // (for bf16 -> FP8 one 1024-column part of it, for a same-dtype copy one
-// 4 KB part) from HBM once, quantises it once (the code of a row does not
+// 2 KB part) from HBM once, quantises it once (the code of a row does not
 // depend on which expert receives it) and stores it to each of its local
 // slots.  A 128-column FP8
 // group is covered by 16 lanes of 8 values (bf16 input) or 32 lanes of 4
 // values (fp32 input); its amax is a butterfly max inside those lanes.
 // Tokens without a local route read nothing.
+//
+// The bf16 and copy kernels run one wave per workgroup and read the token
+// rows with ordinary (cache-allocating) loads: measured inside the whole
+// layer on MI355X, both beat four-wave workgroups and non-temporal loads.
+// Copies store non-temporally: ordinary stores shorten the copy but leave
+// dirty lines that the next GEMM then pays for, with no net gain.
 
 #include "moe_common.h"
 
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 256;                 // fp32 -> FP8 kernel
 constexpr int kTokPerBlock = kThreads / MOE_WAVE;
 constexpr int kUnroll = 16;          // 16-byte chunks per lane in flight (a 4096-column fp32 row)
 
@@ -101,19 +107,18 @@ __global__ __launch_bounds__(kThreads) void permute_f32_fp8_kernel(const float* 
   }
 }
 
-// Same-dtype copy (bf16 or fp32): one wave per (token, 4 KB part of its
-// row); lane l moves the 16-byte chunks 256p + 64u + l, so each load and
+// Same-dtype copy (bf16 or fp32): one wave per (token, 2 KB part of its
+// row); lane l moves the 16-byte chunks 128p + 64u + l, so each load and
 // store instruction covers 1 KB of a row contiguously.
-constexpr int kCopyLoads = 4;
+constexpr int kCopyLoads = 2;
 constexpr int kCopyChunks = kCopyLoads * MOE_WAVE;
 
-__global__ __launch_bounds__(kThreads) void permute_copy_kernel(const uint8_t* __restrict__ x, int T, int K,
+__global__ __launch_bounds__(MOE_WAVE) void permute_copy_kernel(const uint8_t* __restrict__ x, int T, int K,
                                                                int row_bytes, const int32_t* __restrict__ slot_of,
                                                                int64_t rows_cap, uint8_t* __restrict__ buf,
                                                                int parts) {
-  const int wave = threadIdx.x / MOE_WAVE;
   const int lane = moe::lane_id();
-  const int item = blockIdx.x * kTokPerBlock + wave;     // (token, part)
+  const int item = blockIdx.x;                            // (token, part)
   const int t = item / parts;
   const int p = item - t * parts;
   if (t >= T) return;
@@ -126,7 +131,7 @@ __global__ __launch_bounds__(kThreads) void permute_copy_kernel(const uint8_t* _
 #pragma unroll
   for (int u = 0; u < kCopyLoads; ++u) {
     const int c = p * kCopyChunks + u * MOE_WAVE + lane;
-    raw[u] = c < nchunk ? moe::load_nt16(xrow + c) : make_uint4(0, 0, 0, 0);
+    raw[u] = c < nchunk ? xrow[c] : make_uint4(0, 0, 0, 0);
   }
   for (uint64_t m = routes; m; m &= m - 1) {
     const int s = __builtin_amdgcn_readlane(s_l, __builtin_ctzll(m));
@@ -148,14 +153,13 @@ __global__ __launch_bounds__(kThreads) void permute_copy_kernel(const uint8_t* _
 constexpr int kPartLoads = 2;                       // 16-byte chunks per lane
 constexpr int kPartChunks = kPartLoads * MOE_WAVE;  // 8-column chunks per part
 
-__global__ __launch_bounds__(kThreads) void permute_bf16_fp8_kernel(const uint16_t* __restrict__ x, int T,
+__global__ __launch_bounds__(MOE_WAVE) void permute_bf16_fp8_kernel(const uint16_t* __restrict__ x, int T,
                                                                    int K, int H,
                                                                    const int32_t* __restrict__ slot_of,
                                                                    int64_t rows_cap, uint8_t* __restrict__ buf,
                                                                    float* __restrict__ scales, int parts) {
-  const int wave = threadIdx.x / MOE_WAVE;
   const int lane = moe::lane_id();
-  const int item = blockIdx.x * kTokPerBlock + wave;     // (token, part)
+  const int item = blockIdx.x;                            // (token, part)
   const int t = item / parts;
   const int p = item - t * parts;
   if (t >= T) return;
@@ -173,7 +177,7 @@ __global__ __launch_bounds__(kThreads) void permute_bf16_fp8_kernel(const uint16
   for (int h = 0; h < kPartLoads; ++h) {
     c[h] = p * kPartChunks + h * MOE_WAVE + lane;
     live[h] = c[h] < nchunk;
-    raw[h] = live[h] ? moe::load_nt16(xrow + c[h]) : make_uint4(0, 0, 0, 0);
+    raw[h] = live[h] ? xrow[c[h]] : make_uint4(0, 0, 0, 0);
   }
   uint2 codes[kPartLoads];
   float scale[kPartLoads];
@@ -216,8 +220,8 @@ extern "C" moe_status moe_permute(const void* x, moe_dtype x_dt, int T, int K, i
   MOE_CHECK(x && slot_of && buf, MOE_ERR_INVALID_ARG);
   MOE_CHECK(buf_dt != MOE_FP8_E4M3 || buf_scales, MOE_ERR_INVALID_ARG);
   auto* b = static_cast<uint8_t*>(buf);
-  auto item_grid = [&](int parts, int& grid) -> bool {
-    const int64_t g = (static_cast<int64_t>(T) * parts + kTokPerBlock - 1) / kTokPerBlock;
+  auto item_grid = [&](int parts, int per_block, int& grid) -> bool {
+    const int64_t g = (static_cast<int64_t>(T) * parts + per_block - 1) / per_block;
     grid = static_cast<int>(g);
     return g <= 0x7fffffff;
   };
@@ -225,16 +229,16 @@ extern "C" moe_status moe_permute(const void* x, moe_dtype x_dt, int T, int K, i
   if (buf_dt == x_dt) {
     const int row_bytes = H * (x_dt == MOE_BF16 ? 2 : 4);
     const int parts = (row_bytes / 16 + kCopyChunks - 1) / kCopyChunks;
-    MOE_CHECK(item_grid(parts, grid), MOE_ERR_UNSUPPORTED);
-    permute_copy_kernel<<<grid, kThreads, 0, stream>>>(static_cast<const uint8_t*>(x), T, K, row_bytes, slot_of,
+    MOE_CHECK(item_grid(parts, 1, grid), MOE_ERR_UNSUPPORTED);
+    permute_copy_kernel<<<grid, MOE_WAVE, 0, stream>>>(static_cast<const uint8_t*>(x), T, K, row_bytes, slot_of,
                                                        rows_cap, b, parts);
   } else if (x_dt == MOE_BF16) {
     const int parts = (H / 8 + kPartChunks - 1) / kPartChunks;
-    MOE_CHECK(item_grid(parts, grid), MOE_ERR_UNSUPPORTED);
-    permute_bf16_fp8_kernel<<<grid, kThreads, 0, stream>>>(static_cast<const uint16_t*>(x), T, K, H, slot_of,
+    MOE_CHECK(item_grid(parts, 1, grid), MOE_ERR_UNSUPPORTED);
+    permute_bf16_fp8_kernel<<<grid, MOE_WAVE, 0, stream>>>(static_cast<const uint16_t*>(x), T, K, H, slot_of,
                                                            rows_cap, b, buf_scales, parts);
   } else {
-    MOE_CHECK(item_grid(1, grid), MOE_ERR_UNSUPPORTED);
+    MOE_CHECK(item_grid(1, kTokPerBlock, grid), MOE_ERR_UNSUPPORTED);
     permute_f32_fp8_kernel<<<grid, kThreads, 0, stream>>>(static_cast<const float*>(x), T, K, H, slot_of,
                                                           rows_cap, b, buf_scales);
   }
