@@ -12,10 +12,11 @@
 // launched or computed for capacity rows beyond counts[e] (the page's
 // "compact task organisation").  Each workgroup rebuilds the tile map from
 // counts in LDS and walks it persistently; tiles are ordered expert-major,
-// then column block, then row tile, so the row tiles that share a weight
-// block run back to back, and the ordered tile range is cut into 8
-// contiguous chunks, one per XCD (workgroup i runs on XCD i mod 8), so a
-// weight block is fetched from HBM into one XCD's L2 and reused there.
+// then band of 8 row tiles, then column block, then row tile, so the tiles
+// that share a weight block or an activation tile run close together, and
+// the ordered tile range is cut into 8 contiguous chunks, one per XCD
+// (workgroup i runs on XCD i mod 8), so both operands are fetched from HBM
+// into one XCD's L2 and reused there.
 //
 // Tile.  BM = 128 rows x two 128-column "halves" of W rows.  For W13 the
 // halves are the gate block n0 + [0,128) and the matching up block
@@ -76,6 +77,7 @@ constexpr int BH = 128;            // columns per half
 constexpr int KB = 128;            // bytes of K per stage and row
 constexpr int kMaxL = 1024;
 constexpr int NST = 3;             // LDS ring depth
+constexpr int kBand = 8;           // row tiles per band of the tile order
 constexpr int A_BYTES = BM * KB;                   // 16 KB
 constexpr int B_BYTES = 2 * BH * KB;               // 32 KB
 constexpr int AS_BYTES = BM * 4;                   // FP8 activation scales of the stage
@@ -199,8 +201,15 @@ __shared__ float s_amax[4][BM];
 __shared__ int s_part[kThreads];
 
 // Tile id -> (expert, column block, row tile).  s_mt_prefix[e] = sum of row
-// tiles of experts < e; tile ids are expert-major, then column block, then
-// row tile.
+// tiles of experts < e; tile ids are expert-major, then band of kBand row
+// tiles, then column block, then row tile inside the band.  With one
+// workgroup per CU, an XCD's 32 workgroups run 32 consecutive tiles at a
+// time, roughly in step along K: with bands they cover about 8 row tiles x
+// 4 column blocks, so each activation tile and each weight block of the
+// round comes from HBM once and is shared through L2 (the row-tile-inner
+// order alone made the 32 tiles of a large expert share one weight block
+// but stream 32 activation tiles, re-reading every activation tile once per
+// column block).
 __device__ __forceinline__ void decode_tile(int L, int nb_count, int t, int& e, int& nb, int& mt) {
   int lo = 0, hi = L;           // largest e with s_mt_prefix[e]*nb_count <= t
   while (hi - lo > 1) {
@@ -210,8 +219,11 @@ __device__ __forceinline__ void decode_tile(int L, int nb_count, int t, int& e, 
   e = lo;
   const int mte = s_mt_prefix[e + 1] - s_mt_prefix[e];
   const int local = t - s_mt_prefix[e] * nb_count;
-  nb = local / mte;
-  mt = local - nb * mte;
+  const int b = local / (kBand * nb_count);
+  const int r = local - b * kBand * nb_count;
+  const int gm = min(kBand, mte - b * kBand);   // row tiles of this band
+  nb = r / gm;
+  mt = b * kBand + (r - nb * gm);
 }
 
 // One work item, workgroup-uniform: a tile, or one K-range piece of it.
