@@ -447,6 +447,9 @@ def main():
                       "K-split piece reduce included when it runs)")
     roof["timing"] = ("mean over the timed steps of HIP events recorded right before and after the "
                       "gate/up GEMM call on the kernels' stream")
+    # in timed-step order: after a short warm-up the first steps run while the
+    # shader clock is still rising, which shows here as a falling sequence
+    roof["per_step_us"] = [round(v, 1) for v in w13_us]
 
     out = {
         "metric": METRIC,
