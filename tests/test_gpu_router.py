@@ -64,9 +64,9 @@ def test_router_small_all_tokens(ep, E, K, mode):
 @pytest.mark.parametrize("E,K,T", [(256, 8, 16384), (200, 16, 16400), (128, 16, 1000), (64, 6, 1001)])
 @pytest.mark.parametrize("mode", ["bias", "ties"])
 def test_router_segmented_kernel(ep, E, K, T, mode):
-    """Shapes that take the 16-lane-segment kernel (E <= 128, or E <= 256 with
-    at least 16384 tokens), with a token count that leaves the last wave's
-    segments partly empty: ids exact, weights to the bar."""
+    """Token counts that leave the last wave's segments partly empty, on the
+    16-lane-segment kernel (E <= 128) and, at E = 200 and 256, on the
+    wave-per-token kernel at large T: ids exact, weights to the bar."""
     announce("router seg", E, K, T, mode)
     rng = np.random.default_rng(E * 7 + K + T)
     x = rng.standard_normal((T, E)).astype(np.float32)
@@ -85,6 +85,29 @@ def test_router_special_values(ep):
     rid, _ = router.router_topk(x, 8)
     assert np.array_equal(ids, rid)               # inf, 1 (id 4), 1 (id 5), 0 (id 2), -0 (id 3), -1, -inf, nan
     assert list(ids[0]) == [7, 4, 5, 2, 3, 6, 1, 0]
+
+
+@pytest.mark.parametrize("E,K", [(256, 16), (200, 8), (1024, 64)])
+def test_router_special_values_wave_kernel(ep, E, K):
+    """NaN, +-inf and +-0 among ordinary scores on the wave-per-token kernel
+    (E > 128): NaN ranks below every number and goes to the lower id among
+    NaNs, -0 ties +0, the lower id wins a tie; ids exact against the
+    oracle."""
+    announce("router special values, wave kernel", E, K)
+    rng = np.random.default_rng(E + K)
+    x = (np.round(rng.standard_normal((64, E)) * 2) / 2).astype(np.float32)
+    specials = np.array([np.nan, np.inf, -np.inf, 0.0, -0.0], np.float32)
+    for t in range(64):
+        pos = rng.choice(E, size=12, replace=False)
+        x[t, pos] = specials[rng.integers(0, len(specials), size=12)]
+    x[0, :] = np.nan                                # every score NaN: ids 0..K-1
+    x[1, :] = 0.0
+    x[1, ::2] = -0.0                                # every score zero
+    ids, w = run(ep, x, K)
+    rid, _ = router.router_topk(x, K)
+    assert np.array_equal(ids, rid)
+    assert list(ids[0]) == list(range(K))
+    assert list(ids[1]) == list(range(K))
 
 
 @pytest.mark.parametrize("name", ["prefill_fp8", "skewed_bf16"])
