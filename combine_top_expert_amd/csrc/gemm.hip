@@ -29,9 +29,7 @@
 // bytes land at base + size*l), so a wave held at a load issue by the
 // memory pipeline never holds up matrix work.  Waves 0-7 are consumers in
 // a 2 x 4 grid, each owning 64 rows x (32 columns of each half) = 16 MFMA
-// 16x16 tiles; they only read LDS and multiply.  In an expert's only row
-// tile (decode) they skip the products of their 16-row blocks that lie
-// wholly past the tile's valid rows.
+// 16x16 tiles; they only read LDS and multiply.
 //
 // K loop.  One stage = 128 bytes of K per row: 128 FP8, 64 bf16 or 32 fp32
 // values -- for FP8 exactly one activation / weight scale group.  Each
@@ -235,7 +233,6 @@ struct Tile {
   bool half1;
   int ws0, ws1;                        // FP8: first weight-scale index of each half
   int ks0, nks;                        // K stages [ks0, ks0 + nks)
-  bool solo;                           // the expert's only row tile
   int split;                           // -1: whole tile; else the piece's index
 };
 
@@ -337,7 +334,6 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs p) {
     c.e = __builtin_amdgcn_readfirstlane(e);
     c.nb = __builtin_amdgcn_readfirstlane(nb);
     mt = __builtin_amdgcn_readfirstlane(mt);
-    c.solo = s_mt_prefix[c.e + 1] - s_mt_prefix[c.e] == 1;
     const int64_t off = uniform_load(p.offsets, c.e);
     c.rows_valid = min(BM, eff_count(off, uniform_load(p.counts, c.e), p.rows_cap) - mt * BM);
     c.row0 = off + static_cast<int64_t>(mt) * BM;
@@ -546,13 +542,6 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs p) {
     const int nb = cur.nb, rows_valid = cur.rows_valid, n0 = cur.n0;
     const int64_t row0 = cur.row0;
     const bool half1 = cur.half1;
-    // 16-row blocks of this consumer that hold a valid row (a prefix).  Only
-    // an expert's only row tile skips the others: the row tiles of a larger
-    // expert share each weight block through L2 by running in step, and a
-    // short last tile that skipped its padding products would run ahead of
-    // its siblings and fetch the weights alone (measured: 48 % more HBM
-    // reads at the prefill shape)
-    const int nlive = cur.solo ? __builtin_amdgcn_readfirstlane(min(4, max(0, (rows_valid - 64 * wm + 15) / 16))) : 4;
 
     v4f acc[4][2][2];
 #pragma unroll
@@ -596,28 +585,22 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs p) {
         // product n + 2, far enough behind product n for its result to be
         // ready without a stall (one product ahead, every fold waits on the
         // matrix op issued just before it).  Scheduling fences pin the order.
-        // Row blocks past the tile's valid rows (block i >= nlive) are
-        // skipped, products and folds alike.
         const v4f zero = {0.f, 0.f, 0.f, 0.f};
         v4f pr[3];
         float f = 0.f;
-        if (nlive > 0) {
-          pr[0] = mma_stage<DT>(bf[0][0], af[0], zero);
-          pr[1] = mma_stage<DT>(bf[0][1], af[0], zero);
-        }
+        pr[0] = mma_stage<DT>(bf[0][0], af[0], zero);
+        pr[1] = mma_stage<DT>(bf[0][1], af[0], zero);
 #pragma unroll
         for (int n = 0; n < 16; ++n) {
           if (n + 2 < 16) {
             const int m = n + 2;
-            if ((m >> 2) < nlive) pr[m % 3] = mma_stage<DT>(bf[(m >> 1) & 1][m & 1], af[m >> 2], zero);
+            pr[m % 3] = mma_stage<DT>(bf[(m >> 1) & 1][m & 1], af[m >> 2], zero);
           }
           __builtin_amdgcn_sched_barrier(0);
           const int i = n >> 2, h = (n >> 1) & 1, j = n & 1;
-          if (i < nlive) {
-            if (j == 0) f = __int_as_float(sa[i]) * sw[h];
+          if (j == 0) f = __int_as_float(sa[i]) * sw[h];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) acc[i][h][j][r] = fmaf(pr[n % 3][r], f, acc[i][h][j][r]);
-          }
+          for (int r = 0; r < 4; ++r) acc[i][h][j][r] = fmaf(pr[n % 3][r], f, acc[i][h][j][r]);
           __builtin_amdgcn_sched_barrier(0);
         }
       } else {
@@ -626,8 +609,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs p) {
 #pragma unroll
           for (int j = 0; j < 2; ++j)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-              if (i < nlive) acc[i][h][j] = mma_stage<DT>(bf[h][j], af[i], acc[i][h][j]);
+            for (int i = 0; i < 4; ++i) acc[i][h][j] = mma_stage<DT>(bf[h][j], af[i], acc[i][h][j]);
       }
       MOE_BARRIER_ACC(acc);
     }
