@@ -763,6 +763,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs p) {
 // half-wave of 32 lanes takes one row, 4 columns per lane per half.
 constexpr int kReduceThreads = 256;
 constexpr int kReduceRows = 2 * (kReduceThreads / MOE_WAVE);   // rows per block
+constexpr int kReduceBatch = 8;                                 // pieces loaded before adding
 
 template <int EPI>
 __global__ __launch_bounds__(kReduceThreads) void gemm_piece_reduce_kernel(GemmArgs p) {
@@ -776,13 +777,24 @@ __global__ __launch_bounds__(kReduceThreads) void gemm_piece_reduce_kernel(GemmA
   const int c4 = 4 * (lane & 31);
   const int r = blockIdx.y * kReduceRows + 2 * (threadIdx.x / MOE_WAVE) + (lane >> 5);
   if (r < rows_valid) {
+    // pieces are added in order 0, 1, ..., S-1; the loads of a batch of
+    // kReduceBatch pieces are all issued before the first add, so a thread
+    // waits for one memory round trip per batch rather than per piece
+    const float* src = p.part + static_cast<int64_t>(blockIdx.x) * kPartFloats + r * (2 * BH) + c4;
+    const int64_t pstride = static_cast<int64_t>(bstride) * kPartFloats;
     v4f g[2];
+    for (int k0 = 0; k0 < S; k0 += kReduceBatch) {
+      v4f v[kReduceBatch][2];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const float* src = p.part + static_cast<int64_t>(blockIdx.x) * kPartFloats + r * (2 * BH) + h * BH + c4;
-      g[h] = *reinterpret_cast<const v4f*>(src);
-      for (int k = 1; k < S; ++k)
-        g[h] += *reinterpret_cast<const v4f*>(src + static_cast<int64_t>(k) * bstride * kPartFloats);
+      for (int u = 0; u < kReduceBatch; ++u)
+        if (k0 + u < S)
+#pragma unroll
+          for (int h = 0; h < 2; ++h) v[u][h] = *reinterpret_cast<const v4f*>(src + (k0 + u) * pstride + h * BH);
+#pragma unroll
+      for (int u = 0; u < kReduceBatch; ++u)
+        if (k0 + u < S)
+#pragma unroll
+          for (int h = 0; h < 2; ++h) g[h] = (k0 + u == 0) ? v[u][h] : g[h] + v[u][h];
     }
     if constexpr (EPI == EPI_STORE_F32 || EPI == EPI_STORE_BF16) {
 #pragma unroll
