@@ -1086,15 +1086,18 @@ extern "C" moe_status moe_grouped_gemm_w2_combine(const void* z, moe_dtype z_dt,
             MOE_ERR_UNSUPPORTED);
   MOE_CHECK(z_dt != MOE_FP8_E4M3 || I <= 128 * 128, MOE_ERR_UNSUPPORTED);
   if (T == 0) return MOE_OK;
+  // every argument is checked before the first launch
   MOE_CHECK(y_acc && y, MOE_ERR_INVALID_ARG);
   MOE_CHECK(((reinterpret_cast<uintptr_t>(y_acc) | reinterpret_cast<uintptr_t>(y)) & 15) == 0, MOE_ERR_INVALID_ARG);
+  if (rows_cap > 0) {
+    MOE_CHECK(z && w2 && counts && offsets && row_src && topk_weights, MOE_ERR_INVALID_ARG);
+    MOE_CHECK(z_dt != MOE_FP8_E4M3 || (z_scales && w2_scales), MOE_ERR_INVALID_ARG);
+  }
   const int64_t n4 = static_cast<int64_t>(T) * H / 4;
   const int fill_grid = static_cast<int>(std::min<int64_t>((n4 + 255) / 256, 8192));
   zero_f32_kernel<<<fill_grid, 256, 0, stream>>>(y_acc, n4);
   MOE_LAUNCH_CHECK();
   if (rows_cap > 0) {
-    MOE_CHECK(z && w2 && counts && offsets && row_src && topk_weights, MOE_ERR_INVALID_ARG);
-    MOE_CHECK(z_dt != MOE_FP8_E4M3 || (z_scales && w2_scales), MOE_ERR_INVALID_ARG);
     GemmArgs g{};
     g.A = static_cast<const uint8_t*>(z);
     g.As = z_scales;

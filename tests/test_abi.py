@@ -284,3 +284,31 @@ def test_layout_noalloc_argument_errors(lib):
     assert ws(1 << 20, 8, 1024) > mx()
     assert call(T=1 << 20, K=8, E=1024, L=1024) == WORKSPACE
     assert ws(1 << 21, 8, 32) <= mx()                # 16M routes at L = 32 fit
+
+
+def test_w2_combine_argument_errors(lib):
+    """The down GEMM with the combine in its epilogue checks every argument,
+    pointers included, before its first launch (the y_acc clear)."""
+    f = lib.moe_grouped_gemm_w2_combine
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int64,
+                  ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+
+    def call(z_dt=2, w_dt=2, scales=True, L=2, rows_cap=256, H=256, I=128, row_src=True, T=4, K=2,
+             y_acc=16, y=16, y_dt=1):
+        s = P() if scales else None
+        return f(P(), z_dt, s, P(), w_dt, s, P(), P(), L, rows_cap, H, I, P() if row_src else None,
+                 P(), T, K, P(y_acc) if y_acc else None, P(y) if y else None, y_dt, None)
+
+    assert call(z_dt=1) == UNSUPPORTED               # Z and W2 in different formats
+    assert call(H=200) == UNSUPPORTED                 # H % 128
+    assert call(I=100) == UNSUPPORTED                 # I % 128
+    assert call(y_dt=2) == UNSUPPORTED                # y in FP8
+    assert call(L=0) == INVALID
+    assert call(K=0) == INVALID
+    assert call(y_acc=0) == INVALID
+    assert call(y=24) == INVALID                      # y not 16-byte aligned
+    assert call(row_src=False) == INVALID             # rows without their (t, k)
+    assert call(scales=False) == INVALID              # FP8 without block scales
