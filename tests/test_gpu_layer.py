@@ -62,7 +62,8 @@ def run_share(ep, layer, wl):
 @pytest.mark.parametrize("fused", [True, False])
 @pytest.mark.parametrize("name", ["toy_fp32", "share_bf16", "toy_bf16_fp8w", "decode_fp8_small",
                                   "prefill_fp8_small", "skewed_bf16_small", "manyrow_bf16_small",
-                                  "manyrow_fp8_small", "manyrow_fp32_small"])
+                                  "manyrow_fp8_small", "manyrow_fp32_small", "manyexpert_fp8_small",
+                                  "manyexpert_bf16_small"])
 def test_layer_small_all_tokens(ep, name, fused):
     announce("layer", name, "fused" if fused else "unfused")
     wl = make_workload(name)

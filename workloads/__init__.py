@@ -128,6 +128,18 @@ CONFIGS.update({
         bias="zipf", bias_alpha=1.2),
 })
 
+# The largest local expert count (L = 1024, the library's limit) with about
+# two rows per expert: one short row tile per expert, many empty experts,
+# and ids on both sides of the owned range [512, 1536) of 2048.
+CONFIGS.update({
+    "manyexpert_fp8_small": CONFIGS["prefill_fp8"].scaled(
+        name="manyexpert_fp8_small", T=512, K=8, E=2048, expert_begin=512, L=1024, H=256, I=128,
+        R=16, bias="none"),
+    "manyexpert_bf16_small": CONFIGS["skewed_bf16"].scaled(
+        name="manyexpert_bf16_small", T=512, K=8, E=2048, expert_begin=512, L=1024, H=256, I=128,
+        R=0, bias="none"),
+})
+
 
 def get_config(name: str) -> MoEConfig:
     return CONFIGS[name]
