@@ -122,9 +122,9 @@ def test_gemm_argument_errors(lib):
                     ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
 
     def call(a_dt=2, w_dt=2, H=256, I=128, epi=1, out_dt=2, L=2, scales=True, ws=None, ws_bytes=0,
-             layout=0):
+             layout=0, rows_cap=256):
         s = P() if scales else None
-        return w13(P(), a_dt, s, P(), w_dt, s, layout, P(), P(), L, 256, H, I, epi, P(), out_dt, s, ws,
+        return w13(P(), a_dt, s, P(), w_dt, s, layout, P(), P(), L, rows_cap, H, I, epi, P(), out_dt, s, ws,
                    ws_bytes, None)
 
     assert call(a_dt=1, w_dt=2) == UNSUPPORTED
@@ -136,6 +136,11 @@ def test_gemm_argument_errors(lib):
     assert call(scales=False) == INVALID
     assert call(ws=P(), ws_bytes=64) == WORKSPACE     # a workspace below the query's size
     assert call(layout=2) == INVALID                  # unknown weight layout
+    # staged loads use 32-bit buffer offsets: A and one expert's W below 2 GiB
+    assert call(H=16384, rows_cap=131072) == UNSUPPORTED            # A: 16 KiB x 131200 rows
+    assert call(H=16384, I=65536, rows_cap=256) == UNSUPPORTED      # W13[e]: 131072 x 16 KiB
+    assert call(a_dt=1, w_dt=1, H=16384, scales=False, rows_cap=65536) == UNSUPPORTED   # bf16 A
+    assert call(H=16384 + 128) == UNSUPPORTED                       # FP8 K beyond 128 scale groups
     pk = lib.moe_pack_w13
     pk.restype = ctypes.c_int
     pk.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
