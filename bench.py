@@ -210,6 +210,8 @@ def backward_timing(cfg, layer, x, ids, w, steps, dev):
     dy = torch.randn(cfg.T, cfg.H, device=dev, generator=g).to(layer.out.dtype)
     layer.forward(x, ids, w)
     us, total, us_p = _time_stages(layer.backward_stages(dy, w), steps, dev)
+    # the same backward with G stored in fp32 and a separate SiLU*up backward
+    us_sep, total_sep, _ = _time_stages(layer.backward_stages(dy, w, fuse_silu=False), steps, dev)
     tr_us, _, _ = _time_stages([("transpose_weights", layer.refresh_transposed_weights)], steps, dev)
     # unfused forward keeping G, then the backward without the recompute
     layer.set_fused(False)
@@ -224,7 +226,7 @@ def backward_timing(cfg, layer, x, ids, w, steps, dev):
     rows = int(layer.counts.cpu().numpy().sum())
     T, K, H, I = cfg.T, cfg.K, cfg.H, cfg.I
     tok_local = int((layer.slot_of.cpu().numpy() >= 0).any(axis=1).sum())
-    flops = {"gemm_dz": 2 * rows * H * I, "gemm_g": 4 * rows * H * I, "gemm_da": 4 * rows * H * I,
+    flops = {"gemm_dz": 2 * rows * H * I, "gemm_g_silu_bw": 4 * rows * H * I, "gemm_da": 4 * rows * H * I,
              "wgrad_w2": 2 * rows * H * I, "wgrad_w13": 4 * rows * H * I}
     nbytes = {
         # dy once per token with a local route, out rows in, d_out rows out, ids/weights/d_w
@@ -239,9 +241,13 @@ def backward_timing(cfg, layer, x, ids, w, steps, dev):
            "transpose_weights_us": tr_us["transpose_weights"],
            "transpose_note": "W2^T and W13^T, written once per weight update (not part of a pass)",
            "timing": "medians over the passes, an event between stages; after the fused forward "
-                     "(G recomputed)",
-           "tflops": {k: v / (us[k] * 1e-6) / 1e12 for k, v in flops.items()},
-           "gbs": {k: v / (us[k] * 1e-6) / 1e9 for k, v in nbytes.items()},
+                     "(G recomputed by the gate/up GEMM with the SiLU*up gradient in its epilogue)",
+           "tflops": {k: v / (us[k] * 1e-6) / 1e12 for k, v in flops.items() if k in us},
+           "gbs": {k: v / (us[k] * 1e-6) / 1e9 for k, v in nbytes.items() if k in us},
+           "separate_silu": {"us": {k: us_sep[k] for k in ("gemm_g", "silu_mul_bw")},
+                             "backward_total_us": total_sep,
+                             "note": "G stored in fp32 by the gate/up GEMM, then a separate SiLU*up "
+                                     "backward (same results, bit for bit)"},
            "saved_g": {"backward_us": us_saved, "backward_total_us": total_saved,
                        "forward_unfused_us": fwd_us,
                        "note": "unfused forward (gate/up GEMM storing fp32 G, then SiLU*up) keeps G; "

@@ -23,7 +23,8 @@ __all__ = [
     "moe_status_string", "moe_abi_version", "moe_dispatch_layout_workspace_bytes",
     "moe_grouped_gemm_workspace_bytes", "moe_pack_w13", "MOE_W_ROW_MAJOR", "MOE_W_PACKED",
     "moe_combine_backward", "moe_silu_mul_backward", "moe_permute_backward", "moe_transpose_weights",
-    "moe_grouped_gemm_wgrad", "moe_dispatch_layout", "moe_dispatch_layout_noalloc",
+    "moe_grouped_gemm_wgrad", "moe_grouped_gemm_w13_silu_backward", "moe_dispatch_layout",
+    "moe_dispatch_layout_noalloc",
     "moe_dispatch_layout_noalloc_max_bytes", "moe_permute", "moe_grouped_gemm_w13", "moe_silu_mul",
     "moe_grouped_gemm_w2", "moe_grouped_gemm_w2_combine", "moe_combine", "moe_router_topk",
     "dtype_code",
@@ -66,6 +67,8 @@ _SIG = {
     "moe_permute_backward": (_i, [_p, _i, _p, _i, _i, _i, _i64, _p, _i, _p]),
     "moe_transpose_weights": (_i, [_p, _i, _i, _i, _i, _p, _p]),
     "moe_grouped_gemm_wgrad": (_i, [_p, _p, _i, _p, _p, _i, _i64, _i, _i, _p, _p]),
+    "moe_grouped_gemm_w13_silu_backward": (_i, [_p, _i, _p, _i, _i, _p, _p, _i, _i64, _i, _i, _p, _i, _p, _i,
+                                                _p, _sz, _p]),
 }
 for _name, (_res, _args) in _SIG.items():
     if not hasattr(lib, _name):
@@ -282,6 +285,25 @@ def moe_grouped_gemm_w13(a, a_scales, w13, w13_scales, counts, offsets, epi, out
         dtype_code(w13), _f32(w13_scales, "w13_scales"), int(w13_layout), _i32(counts, "counts"),
         _i32(offsets, "offsets"), L, a.shape[0], H, N // 2, int(epi), _ptr(out, "out"),
         dtype_code(out), _f32(out_scales, "out_scales"), wp, wb, _stream(a)))
+
+
+def moe_grouped_gemm_w13_silu_backward(a, w13, counts, offsets, dz, dg, workspace=None,
+                                       w13_layout=MOE_W_ROW_MAJOR, bind=False):
+    """a [rows_cap,H], w13 [L,2I,H] (bf16|fp32), dz [rows_cap,I] -> dg
+    [rows_cap,2I]: G recomputed with the SiLU*up gradient in the GEMM's
+    epilogue (same values as MOE_EPI_STORE_G followed by moe_silu_mul_backward)."""
+    L, N, H = w13.shape
+    rows_cap, I = a.shape[0], N // 2
+    _shape(a, "a", rows_cap, H)
+    _shape(counts, "counts", L)
+    _offsets(offsets, L)
+    _shape(dz, "dz", rows_cap, I)
+    _shape(dg, "dg", rows_cap, N)
+    wp, wb = _ws(workspace)
+    return _run("moe_grouped_gemm_w13_silu_backward", bind, (
+        _ptr(a, "a"), dtype_code(a), _ptr(w13, "w13"), dtype_code(w13), int(w13_layout),
+        _i32(counts, "counts"), _i32(offsets, "offsets"), L, rows_cap, H, I, _ptr(dz, "dz"), dtype_code(dz),
+        _ptr(dg, "dg"), dtype_code(dg), wp, wb, _stream(a)))
 
 
 def moe_silu_mul(g, counts, offsets, z, z_scales=None, bind=False):

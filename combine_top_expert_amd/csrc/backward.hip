@@ -164,8 +164,8 @@ __global__ __launch_bounds__(kThreads) void combine_backward_bf16_reg_kernel(
 }
 
 // d_gate = dz * up * s * (1 + gate * (1 - s)), d_up = dz * SiLU(gate),
-// s = sigmoid(gate) from the hardware exp2 and reciprocal; one wave per valid
-// row, 4 columns per lane per step.
+// s = sigmoid(gate) (moe::silu_mul_grad); one wave per valid row, 4 columns
+// per lane per step.
 constexpr int kSiluBwBatch = 6;
 template <bool kDzF32, bool kDgF32>
 __global__ __launch_bounds__(kThreads) void silu_mul_backward_kernel(
@@ -213,11 +213,7 @@ __global__ __launch_bounds__(kThreads) void silu_mul_backward_kernel(
       const float ga[4] = {gt[b].x, gt[b].y, gt[b].z, gt[b].w}, ua[4] = {up[b].x, up[b].y, up[b].z, up[b].w};
       float dgate[4], dup[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float s = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(ga[i] * -1.44269504088896341f));
-        dup[i] = z[b][i] * (ga[i] * s);
-        dgate[i] = z[b][i] * ua[i] * s * (1.0f + ga[i] * (1.0f - s));
-      }
+      for (int i = 0; i < 4; ++i) moe::silu_mul_grad(ga[i], ua[i], z[b][i], dgate[i], dup[i]);
       if constexpr (kDgF32) {
         reinterpret_cast<float4*>(drow)[c] = make_float4(dgate[0], dgate[1], dgate[2], dgate[3]);
         reinterpret_cast<float4*>(drow + I * 4)[c] = make_float4(dup[0], dup[1], dup[2], dup[3]);

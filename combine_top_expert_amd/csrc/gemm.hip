@@ -88,7 +88,7 @@ static_assert(STAGE % 16 == 0, "stage slots must stay 16-byte aligned");
 
 enum Dt { DT_F32 = 0, DT_BF16 = 1, DT_FP8 = 2 };
 enum Epi { EPI_STORE_F32 = 0, EPI_STORE_BF16 = 1, EPI_SILU_F32 = 2, EPI_SILU_BF16 = 3, EPI_SILU_FP8 = 4,
-           EPI_SCATTER_F32 = 5 };
+           EPI_SCATTER_F32 = 5, EPI_SILU_BWD = 6 };
 
 struct GemmArgs {
   const uint8_t* A;      // [rows_cap, K] elements
@@ -110,6 +110,10 @@ struct GemmArgs {
   float* part;           // K-split partial sums [grid][BM][2*BH] fp32, or null (no split)
   int* desc;             // [grid][kDescInts]: the K-split piece each workgroup ran
   int w_packed;          // W in the packed layout (moe_pack_w13), else [L, N, K]
+  // EPI_SILU_BWD (gate/up GEMM recomputing G for the SiLU*up backward):
+  const uint8_t* dz;         // [rows_cap, I] dZ, fp32 (dz_f32) or bf16
+  int dz_f32;
+  int out_f32;               // dG in out [rows_cap, 2I]: fp32, else bf16
   // EPI_SCATTER_F32 (down GEMM adding weighted rows into token sums):
   const int32_t* row_src;    // [rows_cap]: t * topk + k of each valid row
   const float* route_w;      // [T, topk] router weights
@@ -688,6 +692,56 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs p) {
           }
         }
       }
+    } else if constexpr (EPI == EPI_SILU_BWD) {
+      // dG of the tile's 128 Z columns from its gate and up sums and dZ:
+      // gate gradients to dG columns nb*128 + c, up gradients to I + nb*128 + c.
+      // Every dZ load of the tile is issued before the first is used.
+      const int64_t zcol = static_cast<int64_t>(nb) * BH + ncol;
+      float dz[4][2][4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = mrow + 16 * i;
+        const int64_t q = row0 + min(row, rows_valid - 1);     // rows past the valid ones read a valid row
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          if (p.dz_f32) {
+            const v4f v = *reinterpret_cast<const v4f*>(p.dz + (q * (p.ldo / 2) + zcol + 16 * j) * 4);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) dz[i][j][r] = v[r];
+          } else {
+            const uint2 v = *reinterpret_cast<const uint2*>(p.dz + (q * (p.ldo / 2) + zcol + 16 * j) * 2);
+            dz[i][j][0] = __uint_as_float(v.x << 16);
+            dz[i][j][1] = __uint_as_float(v.x & 0xffff0000u);
+            dz[i][j][2] = __uint_as_float(v.y << 16);
+            dz[i][j][3] = __uint_as_float(v.y & 0xffff0000u);
+          }
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = mrow + 16 * i;
+        if (row >= rows_valid) continue;
+        const int64_t o = (row0 + row) * p.ldo + zcol;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          float dgt[4], dup[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) moe::silu_mul_grad(acc[i][0][j][r], acc[i][1][j][r], dz[i][j][r], dgt[r], dup[r]);
+          if (p.out_f32) {
+            float* d = static_cast<float*>(p.out) + o + 16 * j;
+            *reinterpret_cast<v4f*>(d) = v4f{dgt[0], dgt[1], dgt[2], dgt[3]};
+            *reinterpret_cast<v4f*>(d + p.half_stride) = v4f{dup[0], dup[1], dup[2], dup[3]};
+          } else {
+            uint16_t* d = static_cast<uint16_t*>(p.out) + o + 16 * j;
+            *reinterpret_cast<uint2*>(d) = make_uint2(
+                static_cast<uint32_t>(moe::f32_to_bf16(dgt[0])) | (static_cast<uint32_t>(moe::f32_to_bf16(dgt[1])) << 16),
+                static_cast<uint32_t>(moe::f32_to_bf16(dgt[2])) | (static_cast<uint32_t>(moe::f32_to_bf16(dgt[3])) << 16));
+            *reinterpret_cast<uint2*>(d + p.half_stride) = make_uint2(
+                static_cast<uint32_t>(moe::f32_to_bf16(dup[0])) | (static_cast<uint32_t>(moe::f32_to_bf16(dup[1])) << 16),
+                static_cast<uint32_t>(moe::f32_to_bf16(dup[2])) | (static_cast<uint32_t>(moe::f32_to_bf16(dup[3])) << 16));
+          }
+        }
+      }
     } else {
       // Z = SiLU(gate) * up, columns nb*128 + [0,128) of Z
       float z[4][2][4];
@@ -808,6 +862,36 @@ __global__ __launch_bounds__(kReduceThreads) void gemm_piece_reduce_kernel(GemmA
               static_cast<uint32_t>(moe::f32_to_bf16(g[h][0])) | (static_cast<uint32_t>(moe::f32_to_bf16(g[h][1])) << 16),
               static_cast<uint32_t>(moe::f32_to_bf16(g[h][2])) | (static_cast<uint32_t>(moe::f32_to_bf16(g[h][3])) << 16));
         }
+      }
+    } else if constexpr (EPI == EPI_SILU_BWD) {
+      const int64_t q = row0 + r;
+      const int64_t zc = q * (p.ldo / 2) + static_cast<int64_t>(nb) * BH + c4;
+      float dz[4];
+      if (p.dz_f32) {
+        const v4f v = *reinterpret_cast<const v4f*>(p.dz + zc * 4);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) dz[k] = v[k];
+      } else {
+        const uint2 v = *reinterpret_cast<const uint2*>(p.dz + zc * 2);
+        dz[0] = __uint_as_float(v.x << 16);
+        dz[1] = __uint_as_float(v.x & 0xffff0000u);
+        dz[2] = __uint_as_float(v.y << 16);
+        dz[3] = __uint_as_float(v.y & 0xffff0000u);
+      }
+      float dgt[4], dup[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) moe::silu_mul_grad(g[0][k], g[1][k], dz[k], dgt[k], dup[k]);
+      const int64_t o = q * p.ldo + static_cast<int64_t>(nb) * BH + c4;
+      if (p.out_f32) {
+        *reinterpret_cast<v4f*>(static_cast<float*>(p.out) + o) = v4f{dgt[0], dgt[1], dgt[2], dgt[3]};
+        *reinterpret_cast<v4f*>(static_cast<float*>(p.out) + o + p.half_stride) = v4f{dup[0], dup[1], dup[2], dup[3]};
+      } else {
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + o) = make_uint2(
+            static_cast<uint32_t>(moe::f32_to_bf16(dgt[0])) | (static_cast<uint32_t>(moe::f32_to_bf16(dgt[1])) << 16),
+            static_cast<uint32_t>(moe::f32_to_bf16(dgt[2])) | (static_cast<uint32_t>(moe::f32_to_bf16(dgt[3])) << 16));
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + o + p.half_stride) = make_uint2(
+            static_cast<uint32_t>(moe::f32_to_bf16(dup[0])) | (static_cast<uint32_t>(moe::f32_to_bf16(dup[1])) << 16),
+            static_cast<uint32_t>(moe::f32_to_bf16(dup[2])) | (static_cast<uint32_t>(moe::f32_to_bf16(dup[3])) << 16));
       }
     } else {
       float z[4];
@@ -999,6 +1083,52 @@ extern "C" moe_status moe_grouped_gemm_w13(const void* a, moe_dtype a_dt, const 
     case MOE_BF16: return dispatch_dt<EPI_SILU_BF16>(a_dt, g, mt, stream);
     default: return dispatch_dt<EPI_SILU_FP8>(a_dt, g, mt, stream);
   }
+}
+
+extern "C" moe_status moe_grouped_gemm_w13_silu_backward(const void* a, moe_dtype a_dt, const void* w13,
+                                                        moe_dtype w_dt, moe_weight_layout w13_layout,
+                                                        const int32_t* counts, const int32_t* offsets, int L,
+                                                        int64_t rows_cap, int H, int I, const void* dz,
+                                                        moe_dtype dz_dt, void* dg, moe_dtype dg_dt,
+                                                        void* workspace, size_t workspace_bytes,
+                                                        hipStream_t stream) {
+  MOE_CHECK(L >= 1 && L <= kMaxL && rows_cap >= 0 && H > 0 && I > 0, MOE_ERR_INVALID_ARG);
+  MOE_CHECK(moe_host::valid_dtype(a_dt) && moe_host::valid_dtype(w_dt) && moe_host::valid_dtype(dz_dt) &&
+                moe_host::valid_dtype(dg_dt),
+            MOE_ERR_INVALID_ARG);
+  MOE_CHECK(w13_layout == MOE_W_ROW_MAJOR || w13_layout == MOE_W_PACKED, MOE_ERR_INVALID_ARG);
+  MOE_CHECK(a_dt == w_dt && a_dt != MOE_FP8_E4M3, MOE_ERR_UNSUPPORTED);
+  MOE_CHECK(dz_dt != MOE_FP8_E4M3 && dg_dt != MOE_FP8_E4M3, MOE_ERR_UNSUPPORTED);
+  MOE_CHECK(H % 128 == 0 && I % 128 == 0, MOE_ERR_UNSUPPORTED);
+  MOE_CHECK(offsets_fit(static_cast<int64_t>(H) * moe_host::elem_bytes(a_dt), 2 * static_cast<int64_t>(I),
+                        rows_cap),
+            MOE_ERR_UNSUPPORTED);
+  if (rows_cap == 0) return MOE_OK;
+  MOE_CHECK(a && w13 && counts && offsets && dz && dg, MOE_ERR_INVALID_ARG);
+  GemmArgs g{};
+  g.A = static_cast<const uint8_t*>(a);
+  g.W = static_cast<const uint8_t*>(w13);
+  g.counts = counts;
+  g.offsets = offsets;
+  g.L = L;
+  g.K = H;
+  g.N = 2 * I;
+  g.nb_count = I / BH;
+  g.nb_stride = BH;
+  g.half_stride = I;
+  g.rows_cap = rows_cap;
+  g.out = dg;
+  g.ldo = 2 * I;
+  g.dz = static_cast<const uint8_t*>(dz);
+  g.dz_f32 = dz_dt == MOE_F32;
+  g.out_f32 = dg_dt == MOE_F32;
+  g.w_packed = w13_layout == MOE_W_PACKED;
+  const int mt = max_row_tiles(rows_cap, L);
+  const moe_status ws_st = bind_workspace(g, mt, moe_host::elem_bytes(a_dt), workspace, workspace_bytes);
+  if (ws_st != MOE_OK) return ws_st;
+  // bf16 and fp32 only: the backward has no FP8 form
+  if (a_dt == MOE_F32) return launch<DT_F32, EPI_SILU_BWD>(g, mt, stream);
+  return launch<DT_BF16, EPI_SILU_BWD>(g, mt, stream);
 }
 
 extern "C" moe_status moe_grouped_gemm_w2(const void* z, moe_dtype z_dt, const float* z_scales,

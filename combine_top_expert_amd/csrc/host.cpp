@@ -36,4 +36,4 @@ extern "C" const char* moe_status_string(int status) {
   }
 }
 
-extern "C" int moe_abi_version(void) { return 8; }
+extern "C" int moe_abi_version(void) { return 9; }

@@ -88,6 +88,18 @@ __device__ __forceinline__ float silu(float v) {
   return v * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
+// Gradient of z = SiLU(g) * u for one element, given dz:
+//   d_up = dz * SiLU(g),  d_gate = dz * u * s * (1 + g * (1 - s)),  s = sigmoid(g),
+// s from the same hardware exp2 and reciprocal as silu().  Contraction is off
+// so that every kernel that calls it (the SiLU*up backward and the gate/up
+// GEMM's backward epilogue) gets the same bits from the same g, u, dz.
+__device__ __forceinline__ void silu_mul_grad(float g, float u, float dz, float& dgate, float& dup) {
+#pragma clang fp contract(off)
+  const float s = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(g * -1.44269504088896341f));
+  dup = dz * (g * s);
+  dgate = dz * u * s * (1.0f + g * (1.0f - s));
+}
+
 // 16-byte loads/stores that bypass cache retention (streamed once)
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ uint4 load_nt16(const void* p) {

@@ -20,7 +20,7 @@ from . import (MOE_EPI_SILU_MUL, MOE_EPI_STORE_G, moe_combine, moe_dispatch_layo
                moe_dispatch_layout_workspace_bytes, moe_grouped_gemm_w2, moe_grouped_gemm_w13,
                moe_grouped_gemm_workspace_bytes, moe_pack_w13, MOE_W_PACKED, MOE_W_ROW_MAJOR,
                moe_combine_backward, moe_silu_mul_backward, moe_permute_backward,
-               moe_transpose_weights, moe_grouped_gemm_wgrad,
+               moe_transpose_weights, moe_grouped_gemm_wgrad, moe_grouped_gemm_w13_silu_backward,
                moe_permute, moe_silu_mul)
 
 _TORCH = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8}
@@ -163,9 +163,6 @@ class MoELayer:
         if getattr(self, "d_out", None) is None:
             self.d_out = torch.empty(rc, s.H, dtype=gdt, device=dev)
             self.d_w = torch.empty(s.T, s.K, dtype=torch.float32, device=dev)
-            # G: the unfused forward keeps it; after the fused forward it is recomputed
-            self.g_saved = (self.g if self.g is not None
-                            else torch.empty(rc, 2 * s.I, dtype=torch.float32, device=dev))
             self.dz = torch.empty(rc, s.I, dtype=gdt, device=dev)
             self.dg = torch.empty(rc, 2 * s.I, dtype=gdt, device=dev)
             self.da = torch.empty(rc, s.H, dtype=gdt, device=dev)
@@ -181,13 +178,17 @@ class MoELayer:
         moe_transpose_weights(self.w2, self.w2_t)
         moe_transpose_weights(self.w13, self.w13_t)
 
-    def backward_stages(self, dy, topk_weights, weight_grads=True):
+    def backward_stages(self, dy, topk_weights, weight_grads=True, fuse_silu=True):
         """The backward as (name, launch) pairs in run order, for dy [T,H]:
-        combine backward, dZ = d_out W2 (on W2^T), G recomputed (only after
-        the fused forward: the unfused one keeps G), SiLU*up backward,
-        dA = dG W13 (on W13^T), permute backward, then with weight_grads
-        dW2 = d_out^T Z and dW13 = dG^T A per expert."""
+        combine backward, dZ = d_out W2 (on W2^T), dG, dA = dG W13 (on
+        W13^T), permute backward, then with weight_grads dW2 = d_out^T Z and
+        dW13 = dG^T A per expert.  dG comes from G and dZ: after the unfused
+        forward, which kept G, the SiLU*up backward reads it; after the fused
+        forward the gate/up GEMM recomputes G with the SiLU*up gradient in its
+        epilogue ("gemm_g_silu_bw"), or, with fuse_silu=False, stores fp32 G
+        (g_saved) for a separate SiLU*up backward (the same values)."""
         self.prepare_backward()
+        s = self.shape
         w, lay = ((self.w13_packed, MOE_W_PACKED) if self.w13_packed is not None
                   else (self.w13, MOE_W_ROW_MAJOR))
         st = [
@@ -195,18 +196,28 @@ class MoELayer:
                                                         self.d_out, self.d_w)),
             ("gemm_dz", lambda: moe_grouped_gemm_w2(self.d_out, None, self.w2_t, None, self.counts,
                                                     self.offsets, self.dz, workspace=self.gemm_workspace)),
-            ("gemm_g", lambda: moe_grouped_gemm_w13(self.buf, self.buf_scales, w, self.w13_scales,
-                                                    self.counts, self.offsets, MOE_EPI_STORE_G,
-                                                    self.g_saved, workspace=self.gemm_workspace,
-                                                    w13_layout=lay)),
-            ("silu_mul_bw", lambda: moe_silu_mul_backward(self.g_saved, self.dz, self.counts,
-                                                          self.offsets, self.dg)),
+        ]
+        if self.g is None and fuse_silu:
+            st.append(("gemm_g_silu_bw", lambda: moe_grouped_gemm_w13_silu_backward(
+                self.buf, w, self.counts, self.offsets, self.dz, self.dg, workspace=self.gemm_workspace,
+                w13_layout=lay)))
+        else:
+            if self.g is not None:
+                self.g_saved = self.g                # kept by the unfused forward
+            else:
+                if getattr(self, "g_saved", None) is None:
+                    self.g_saved = torch.empty(s.rows_cap, 2 * s.I, dtype=torch.float32,
+                                               device=self.buf.device)
+                st.append(("gemm_g", lambda: moe_grouped_gemm_w13(
+                    self.buf, self.buf_scales, w, self.w13_scales, self.counts, self.offsets,
+                    MOE_EPI_STORE_G, self.g_saved, workspace=self.gemm_workspace, w13_layout=lay)))
+            st.append(("silu_mul_bw", lambda: moe_silu_mul_backward(self.g_saved, self.dz, self.counts,
+                                                                    self.offsets, self.dg)))
+        st += [
             ("gemm_da", lambda: moe_grouped_gemm_w2(self.dg, None, self.w13_t, None, self.counts,
                                                     self.offsets, self.da, workspace=self.gemm_workspace)),
             ("permute_bw", lambda: moe_permute_backward(self.da, self.slot_of, self.dx)),
         ]
-        if self.g is not None:
-            st = [x for x in st if x[0] != "gemm_g"]
         if weight_grads:
             st += [
                 ("wgrad_w2", lambda: moe_grouped_gemm_wgrad(self.d_out, self.z, self.counts,
@@ -216,13 +227,13 @@ class MoELayer:
             ]
         return st
 
-    def backward(self, dy, topk_weights, weight_grads=True):
+    def backward(self, dy, topk_weights, weight_grads=True, fuse_silu=True):
         """Gradients of the last forward for dy [T,H]: returns (dx [T,H],
         d_w [T,K]); with weight_grads also fills dw2 [L,H,I] = d_out^T Z and
         dw13 [L,2I,H] = dG^T A per expert.  Reuses the forward's routing
         (slot_of, counts, offsets), its permuted activations, Z and expert
         outputs; G is the unfused forward's, else recomputed."""
-        for _, f in self.backward_stages(dy, topk_weights, weight_grads):
+        for _, f in self.backward_stages(dy, topk_weights, weight_grads, fuse_silu):
             f()
         return self.dx, self.d_w
 

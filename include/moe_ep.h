@@ -81,7 +81,8 @@ const char* moe_status_string(int status);
 
 /* ABI version; bumped on any signature change or added entry point (2: moe_router_topk;
  * 3: GEMM workspace for the K-split last round; 4: moe_pack_w13 and the W13 layout;
- * 5: the backward entry points; 6: moe_grouped_gemm_wgrad; 7: moe_dispatch_layout_noalloc; 8: moe_grouped_gemm_w2_combine). */
+ * 5: the backward entry points; 6: moe_grouped_gemm_wgrad; 7: moe_dispatch_layout_noalloc; 8: moe_grouped_gemm_w2_combine;
+ * 9: moe_grouped_gemm_w13_silu_backward). */
 int moe_abi_version(void);
 
 /* Bytes of device workspace moe_dispatch_layout needs for (T, K, L). */
@@ -386,6 +387,29 @@ moe_status moe_silu_mul_backward(const float* g, const void* dz, moe_dtype dz_dt
                                  const int32_t* counts, const int32_t* offsets, int L,
                                  int64_t rows_cap, int I, void* dg, moe_dtype dg_dt,
                                  hipStream_t stream);
+
+/*
+ * moe_grouped_gemm_w13_silu_backward -- the gate/up GEMM recomputed for the
+ * backward with the SiLU*up gradient in its epilogue: for each valid row q of
+ * expert e, G[q] = A[q] W13[e]^T as in moe_grouped_gemm_w13 (fp32 sums, never
+ * stored), then dG[q] from G[q] and dZ[q] exactly as moe_silu_mul_backward
+ * computes it (same fp32 operations, so the same bits as G stored by
+ * MOE_EPI_STORE_G followed by moe_silu_mul_backward).  The XTuner Domino EP
+ * page's backward consumes the forward's saved routing in reverse order; the
+ * gradient is the derivative of the pages' expert MLP ([ECB] §1.1, §3.6).
+ * Saves writing fp32 G and reading it back when the forward did not keep G.
+ *   a [rows_cap,H], w13 [L,2I,H] (or packed, w13_layout), a_dt = w_dt in
+ *   {F32, BF16};  dz [rows_cap,I] (dz_dt F32 or BF16);  dg [rows_cap,2I]
+ *   (dg_dt F32 or BF16: d_gate in columns [0,I), d_up in [I,2I)).
+ *   counts, offsets, workspace as for moe_grouped_gemm_w13.
+ * Limits: H % 128 == 0, I % 128 == 0, L <= 1024.  Padding rows of dg are left
+ * untouched.
+ */
+moe_status moe_grouped_gemm_w13_silu_backward(const void* a, moe_dtype a_dt, const void* w13, moe_dtype w_dt,
+                                              moe_weight_layout w13_layout, const int32_t* counts,
+                                              const int32_t* offsets, int L, int64_t rows_cap, int H, int I,
+                                              const void* dz, moe_dtype dz_dt, void* dg, moe_dtype dg_dt,
+                                              void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * moe_permute_backward -- the gradient of moe_permute (an unweighted combine):

@@ -38,9 +38,10 @@ def test_header_declares_the_entry_points():
                  "moe_grouped_gemm_workspace_bytes", "moe_pack_w13", "moe_combine_backward",
                  "moe_silu_mul_backward", "moe_permute_backward", "moe_transpose_weights",
                  "moe_grouped_gemm_wgrad", "moe_dispatch_layout_noalloc",
-                 "moe_dispatch_layout_noalloc_max_bytes", "moe_grouped_gemm_w2_combine"]:
+                 "moe_dispatch_layout_noalloc_max_bytes", "moe_grouped_gemm_w2_combine",
+                 "moe_grouped_gemm_w13_silu_backward"]:
         assert name in fns
-    assert len(fns) == 20
+    assert len(fns) == 21
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -59,7 +60,7 @@ def test_status_strings_and_version(lib):
     assert lib.moe_status_string(0) == b"MOE_OK"
     assert lib.moe_status_string(-2) == b"MOE_ERR_UNSUPPORTED"
     assert lib.moe_status_string(12345) == b"MOE_ERR_UNKNOWN"
-    assert lib.moe_abi_version() == 8
+    assert lib.moe_abi_version() == 9
 
 
 def test_workspace_bytes(lib):
@@ -185,7 +186,7 @@ def test_python_binding_loads_and_matches_header(lib):
     import combine_top_expert_amd as ep
     for name in declared_functions():
         assert callable(getattr(ep, name)), name
-    assert ep.moe_abi_version() == 8
+    assert ep.moe_abi_version() == 9
     assert ep.moe_status_string(-1) == "MOE_ERR_INVALID_ARG"
 
 
@@ -262,6 +263,26 @@ def test_backward_argument_errors(lib):
     assert wg(P(258), A, 1, A, A, 4, 64, 128, 128, A, None) == INVALID                  # misaligned b
     assert wg(A, None, 1, A, A, 4, 64, 128, 128, A, None) == INVALID                    # no a
     assert wg(A, A, 1, A, A, 4, 64, 128, 128, P(260), None) == INVALID                  # misaligned c
+    fb = lib.moe_grouped_gemm_w13_silu_backward
+    fb.restype = ctypes.c_int
+    fb.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                   ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                   ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+
+    def fcall(a_dt=1, w_dt=1, dz_dt=1, dg_dt=1, H=256, I=128, L=2, layout=0, dz=True, ws=None, ws_bytes=0):
+        return fb(P(), a_dt, P(), w_dt, layout, P(), P(), L, 256, H, I, P() if dz else None, dz_dt, P(), dg_dt,
+                  ws, ws_bytes, None)
+
+    assert fcall(a_dt=2, w_dt=2) == UNSUPPORTED                                           # no FP8 backward
+    assert fcall(a_dt=0) == UNSUPPORTED                                                   # a_dt != w_dt
+    assert fcall(dz_dt=2) == UNSUPPORTED
+    assert fcall(dg_dt=2) == UNSUPPORTED
+    assert fcall(H=200) == UNSUPPORTED
+    assert fcall(I=100) == UNSUPPORTED
+    assert fcall(L=0) == INVALID
+    assert fcall(layout=2) == INVALID
+    assert fcall(dz=False) == INVALID
+    assert fcall(ws=P(), ws_bytes=64) == WORKSPACE
 
 
 def test_layout_noalloc_argument_errors(lib):

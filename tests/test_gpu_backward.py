@@ -64,7 +64,8 @@ def _run(ep, case):
     dy_vals = B.to_format(dy32, "bf16" if bf else "f32")
     dy = torch.from_numpy(dy_vals).cuda().to(torch.bfloat16 if bf else torch.float32)
     names = [n for n, _ in layer.backward_stages(dy, w)]
-    assert ("gemm_g" in names) == (mode != "saved_g")
+    assert ("gemm_g_silu_bw" in names) == (mode != "saved_g")     # G recomputed with dG in its epilogue
+    assert "gemm_g" not in names
     dx, d_w = layer.backward(dy, w)
     torch.cuda.synchronize()
     return cfg, wl, layer, dy_vals, host_vals(dx), d_w.cpu().numpy()
@@ -93,7 +94,13 @@ def test_backward_stages(ep, name):
     dz = host_vals(layer.dz)
     dg = host_vals(layer.dg)
     da = host_vals(layer.da)
-    g = layer.g_saved.cpu().numpy()
+    a_gpu = host_vals(layer.buf)
+    if layer.g is not None:                      # kept by the unfused forward
+        g = layer.g.cpu().numpy()
+    else:                                        # never stored: float64 G on the GPU's A
+        g = np.zeros((cfg.rows_cap, 2 * cfg.I))
+        for q in rows:
+            g[q] = a_gpu[q].astype(np.float64) @ ew.w13(e_of[int(q)]).T
     dz_ref = np.stack([d_out[q].astype(np.float64) @ ew.w2(e_of[int(q)]) for q in rows])
     da_ref = np.stack([dg[q].astype(np.float64) @ ew.w13(e_of[int(q)]) for q in rows])
     tol = 1e-5 if gdt == "f32" else 4e-3
@@ -201,8 +208,18 @@ def test_backward_full_size_sampled(ep):
     g = torch.Generator(device="cuda")
     g.manual_seed(77)
     dy = torch.randn(cfg.T, cfg.H, device="cuda", generator=g).to(torch.bfloat16)
+    # G recomputed with the SiLU*up gradient in the GEMM's epilogue (K-split
+    # last round included at this shape), then again as stored fp32 G and a
+    # separate SiLU*up backward: every gradient bit-identical
+    names = [n for n, _ in layer.backward_stages(dy, w)]
+    assert "gemm_g_silu_bw" in names and "silu_mul_bw" not in names
     layer.backward(dy, w)
+    fused = {k: getattr(layer, k).clone() for k in ("dg", "da", "dx", "d_w", "dw2", "dw13")}
+    layer.backward(dy, w, fuse_silu=False)
     torch.cuda.synchronize()
+    for k, v in fused.items():
+        assert torch.equal(v, getattr(layer, k)), f"{k}: fused and separate SiLU*up backward differ"
+    del fused
     ew = moe.ExpertWeights(cfg, wl.w, cache=False)
     slot_of = layer.slot_of.cpu().numpy()
     counts, offsets = layer.counts.cpu().numpy(), layer.offsets.cpu().numpy()
@@ -345,3 +362,41 @@ def test_combine_backward_direct(ep, H):
     dw = d_w.cpu().numpy()
     assert np.all(dw[slot_of < 0] == 0)
     assert rel_l2(dw, d_w_ref) < 1e-5
+
+
+@pytest.mark.parametrize("name", ["skewed_bf16_small", "manyrow_fp32_small", "ksplit_bf16"])
+def test_fused_silu_backward_matches_separate(ep, name):
+    """moe_grouped_gemm_w13_silu_backward (G recomputed, dG in the GEMM's
+    epilogue) against MOE_EPI_STORE_G followed by moe_silu_mul_backward on
+    the same inputs: every gradient bit-identical.  ksplit_bf16 splits the
+    gate/up GEMM's last round along K, so the piece reduce's epilogue runs."""
+    from combine_top_expert_amd.pipeline import MoELayer
+    from test_gpu_gemm_combine import gemm_grid, k_split_plan
+    announce("fused SiLU*up backward", name)
+    cfg = (get_config("skewed_bf16_small").scaled(name="ksplit_bf16", T=128, E=8, L=8, H=2048, I=512, R=512)
+           if name == "ksplit_bf16" else get_config(name))
+    wl = make_workload(cfg)
+    layer = MoELayer(layer_shape(cfg))
+    upload_weights(layer, wl)
+    bf = cfg.act == "bf16"
+    x, w = dev(wl.x, "bf16" if bf else None), dev(wl.weights)
+    layer.forward(x, dev(wl.ids), w)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(23)
+    dy = torch.randn(cfg.T, cfg.H, device="cuda", generator=gen).to(layer.out.dtype)
+    if name == "ksplit_bf16":
+        mts = int(sum(-(-int(c) // 128) for c in layer.counts.cpu().numpy()))
+        nb = cfg.I // 128
+        plan = k_split_plan(mts * nb, gemm_grid(cfg.rows_cap, cfg.L, nb), cfg.H * 2 // 128)
+        assert max(S for _, _, S in plan) > 1, plan
+    names = [n for n, _ in layer.backward_stages(dy, w)]
+    assert "gemm_g_silu_bw" in names and "silu_mul_bw" not in names
+    layer.backward(dy, w)
+    fused = {k: getattr(layer, k).clone() for k in ("dg", "da", "dx", "d_w", "dw2", "dw13")}
+    names = [n for n, _ in layer.backward_stages(dy, w, fuse_silu=False)]
+    assert "gemm_g" in names and "silu_mul_bw" in names
+    layer.backward(dy, w, fuse_silu=False)
+    torch.cuda.synchronize()
+    for k, v in fused.items():
+        assert torch.equal(v, getattr(layer, k)), f"{name} {k}: fused and separate backward differ"
+    assert torch.isfinite(layer.dw13).all() and layer.dg.float().abs().sum() > 0
