@@ -418,14 +418,11 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs p) {
     // expert's [N, K] block.  Rows past the end of a resource read as 0, so a
     // tail tile may read past its expert's last row without a clamp; those
     // rows are never stored.
-    const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint8_t*>(p.A), 0, static_cast<int>(p.rows_cap * lda), kRsrcWord3);
+    const int a_records = static_cast<int>(p.rows_cap * lda);
     const __amdgpu_buffer_rsrc_t rS = kFp8 ? __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<float*>(p.As), 0, static_cast<int>(p.rows_cap * kgroups * 4), kRsrcWord3) : rA;
-    const __amdgpu_buffer_rsrc_t rWs = kFp8 ? __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<float*>(p.Ws), 0, p.L * (p.N / 128) * kgroups * 4, kRsrcWord3) : rA;
-    // zero records: every access is out of range, reads zeros, moves nothing
-    const __amdgpu_buffer_rsrc_t rNone = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p.A), 0, 0, kRsrcWord3);
+        const_cast<float*>(p.As), 0, static_cast<int>(p.rows_cap * kgroups * 4), kRsrcWord3)
+                                           : __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p.A), 0, 0,
+                                                                               kRsrcWord3);
     typedef __attribute__((address_space(3))) void* lds_void;
 
     // half 0 / half 1 of this producer's loads of K stage ks of tile c into
@@ -436,20 +433,27 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs p) {
           static_cast<int>(w_expert_bytes), kRsrcWord3);
       uint8_t* st = s_ring + s * STAGE;
       if constexpr (kFp8) {
+        // the two weight-block scales: always in range, so a plain global
+        // load (a 64-bit base) rather than a 4-register buffer resource
         if (half == 0 && pw == 0 && lane < 2)
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(rWs, (lds_void)(st + A_BYTES + B_BYTES + AS_BYTES), 4,
-                                                   (lane ? c.ws1 : c.ws0) * 4, ks * 4, 0, 0);
+          __builtin_amdgcn_global_load_lds(const_cast<float*>(p.Ws) + (lane ? c.ws1 : c.ws0) + ks,
+                                           (lds_void)(st + A_BYTES + B_BYTES + AS_BYTES), 4, 0, 0);
       }
       const int a_off = static_cast<int>((c.row0 + 32 * pw) * lda) + ks * KB;
 #pragma unroll
       for (int jj = 0; jj < 2; ++jj) {
         const int j = 2 * half + jj;
         // 8-row groups wholly past the tile's valid rows (an expert's tail,
-        // most of a decode tile) go to the empty resource: the load still
-        // counts (the vmcnt bookkeeping stays fixed) but touches no memory;
-        // those rows' results are never stored
+        // most of a decode tile) load through a resource of zero records:
+        // the load still counts (the vmcnt bookkeeping stays fixed) but
+        // every access is out of range, reads zeros and touches no memory;
+        // those rows' results are never stored.  The resource is built per
+        // load from the base pointer, so only the pointer and the record
+        // count stay in registers.
         const bool live = 32 * pw + 8 * j < c.rows_valid;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(live ? rA : rNone, (lds_void)(st + (32 * pw + 8 * j) * KB), 16,
+        const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint8_t*>(p.A), 0, live ? a_records : 0, kRsrcWord3);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_void)(st + (32 * pw + 8 * j) * KB), 16,
                                                  (j & 1) ? voff_o : voff_e,
                                                  a_off + static_cast<int>(8 * j * lda), 0, 0);
       }
