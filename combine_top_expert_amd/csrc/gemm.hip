@@ -433,11 +433,12 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs p) {
           static_cast<int>(w_expert_bytes), kRsrcWord3);
       uint8_t* st = s_ring + s * STAGE;
       if constexpr (kFp8) {
-        // the two weight-block scales: always in range, so a plain global
-        // load (a 64-bit base) rather than a 4-register buffer resource
-        if (half == 0 && pw == 0 && lane < 2)
-          __builtin_amdgcn_global_load_lds(const_cast<float*>(p.Ws) + (lane ? c.ws1 : c.ws0) + ks,
-                                           (lds_void)(st + A_BYTES + B_BYTES + AS_BYTES), 4, 0, 0);
+        if (half == 0 && pw == 0 && lane < 2) {
+          const __amdgpu_buffer_rsrc_t rWs = __builtin_amdgcn_make_buffer_rsrc(
+              const_cast<float*>(p.Ws), 0, p.L * (p.N / 128) * kgroups * 4, kRsrcWord3);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rWs, (lds_void)(st + A_BYTES + B_BYTES + AS_BYTES), 4,
+                                                   (lane ? c.ws1 : c.ws0) * 4, ks * 4, 0, 0);
+        }
       }
       const int a_off = static_cast<int>((c.row0 + 32 * pw) * lda) + ks * KB;
 #pragma unroll
