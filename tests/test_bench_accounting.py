@@ -7,6 +7,8 @@ fp32 scales, i.e. 8192, 4096 and 128 bytes per row.  Every reported GB/s and
 roofline fraction rests on these counts."""
 from types import SimpleNamespace
 
+import pytest
+
 import numpy as np
 
 import bench
@@ -56,3 +58,17 @@ def test_permute_and_combine_move_the_valid_rows():
     assert w["w13_bytes"] == active * 256 * H * 2 + 224 * H * 2 + 224 * 128 * 2
     assert w["w13_flops"] == 2 * 224 * H * 256
     assert w["gemm_flops"] == 6 * H * 128 * 224
+
+
+@pytest.mark.parametrize("n", [2, 8])
+def test_bench_refuses_more_than_one_gpu(n):
+    """bench.py measures one GPU's share: --gpus N > 1 exits with status 2 and
+    says why, before touching a GPU."""
+    import subprocess
+    import sys
+    from pathlib import Path
+    root = Path(__file__).resolve().parents[1]
+    r = subprocess.run([sys.executable, str(root / "bench.py"), "--gpus", str(n)], capture_output=True,
+                       text=True, timeout=120, cwd=root)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
